@@ -1,0 +1,99 @@
+/*
+ * libsanala -- ReLU linear self-attention with QK-RMSNorm for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (per sample b, head h, token i), from "Sana: Efficient High-Resolution Image
+ * Synthesis with Linear Diffusion Transformers" (paper notes), section 2.1 "linear attention",
+ * Eq. (1), with the QK Norm of "SANA 1.5: Efficient Scaling of Training-Time and Inference-Time
+ * Compute in Linear Diffusion Transformer" (research notes), section "model architecture":
+ *
+ *   phi(x)   = ReLU( x / sqrt(mean_c x_c^2 + eps) * g )     RMSNorm over all C = H*D channels
+ *   S_h      = sum_j phi(K_j,h)^T V_j,h                      D x D, accumulated in fp32
+ *   z_h      = sum_j phi(K_j,h)                              D, fp32
+ *   O_i,h    = phi(Q_i,h) S_h / ( phi(Q_i,h) . z_h + eps )
+ *
+ * The sum over j is over all N tokens of the sample (non-causal).  Head h owns channels
+ * [h*D, (h+1)*D) of a token row.  The same eps is added inside the RMSNorm square root and to the
+ * attention denominator.  Passing gq = gk = NULL switches the QK-Norm off: phi(x) = ReLU(x).
+ *
+ * Layout: every token tensor is row-major [B, N, C] with C = H*D contiguous channels per token;
+ * gq and gk are fp32 [C].  All tensor pointers are device pointers owned by the caller; the
+ * library never frees or keeps them.  `out` must not overlap any input.
+ *
+ * Calls are asynchronous on `stream` and return without a host synchronisation.  Argument checks
+ * happen on the host before anything is enqueued; faults inside kernels surface at the caller's
+ * next synchronisation.  NaN/Inf in the inputs propagate to the outputs they touch; nothing checks
+ * for them.  Scratch memory (row statistics, split-N partial states, the reduced state, and for the
+ * fused call the qkv buffer) is taken with hipMallocAsync on `stream` and released with
+ * hipFreeAsync on the same stream, so concurrent calls on different streams do not share it.
+ * Results are bitwise reproducible: every reduction runs in a fixed order, with no floating-point
+ * atomics.
+ */
+#ifndef SANALA_H
+#define SANALA_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SANA_OK = 0,
+  SANA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad eps, only one gain NULL, ... */
+  SANA_ERR_UNSUPPORTED = 2, /* a shape or dtype this build has no kernel for (D != 32, ...) */
+  SANA_ERR_MISALIGNED = 3,  /* a tensor pointer is not 16-byte aligned */
+  SANA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} sana_status_t;
+
+typedef enum {
+  SANA_F32 = 0,  /* fp32 storage, fp32 arithmetic */
+  SANA_BF16 = 1  /* bf16 storage; fp32 accumulation; bf16 MFMA operands; outputs rounded to nearest even */
+} sana_dtype_t;
+
+/*
+ * sana_linear_attn_fwd -- O = linear attention of (q, k, v) as defined above.
+ *
+ *   q, k, v  device, [B, N, H*D] of `dtype`, contiguous, 16-byte aligned.
+ *   gq, gk   device, fp32 [H*D]: RMSNorm gains of Q and K; both NULL for QK-Norm off.
+ *   B, N, H  >= 1; D must be 32.  B*N*H*D < 2^40.
+ *   eps      finite, >= 0 (SANA uses 1e-6).
+ *   out      device, [B, N, H*D] of `dtype`, contiguous, 16-byte aligned; fully overwritten.
+ *   stream   HIP stream the work is enqueued on (0 = the null stream).
+ *   dtype    SANA_F32 or SANA_BF16 (storage type of q, k, v and out).
+ *
+ * Returns SANA_OK once the work is enqueued, or an error code with nothing enqueued.
+ */
+sana_status_t sana_linear_attn_fwd(const void* q, const void* k, const void* v,
+                                   const float* gq, const float* gk,
+                                   int B, int N, int H, int D, float eps,
+                                   void* out, hipStream_t stream, sana_dtype_t dtype);
+
+/*
+ * sana_qkv_linear_attn_fwd -- fused front end: qkv = x @ Wqkv (bf16 MFMA GEMM, fp32 accumulation,
+ * qkv rounded to bf16), then sana_linear_attn_fwd on the q | k | v column blocks.  The QKV
+ * projection is the one the Sana notes (section 7, on-device deployment) fuse with ReLU(K)^T V.
+ *
+ *   x        device bf16 [B, N, C], C = H*D, contiguous, 16-byte aligned.
+ *   Wqkv     device bf16 [C, 3C] row-major (x @ Wqkv); columns [0,C) give q, [C,2C) k, [2C,3C) v;
+ *            no bias.
+ *   gq, gk   device fp32 [C], or both NULL (QK-Norm off).
+ *   B, N, H  >= 1; D must be 32.
+ *   eps      finite, >= 0.
+ *   out      device bf16 [B, N, C]; fully overwritten.
+ *   stream   HIP stream.
+ *
+ * The qkv intermediate (B*N*3C bf16) is stream-ordered scratch.  Errors as above.
+ */
+sana_status_t sana_qkv_linear_attn_fwd(const void* x, const void* Wqkv,
+                                       const float* gq, const float* gk,
+                                       int B, int N, int H, int D, float eps,
+                                       void* out, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* sana_status_string(sana_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SANALA_H */

@@ -1,0 +1,12 @@
+"""libsanala: ReLU linear self-attention with QK-RMSNorm (SANA's Linear DiT block) on MI355X.
+
+The compute lives in hand-written HIP kernels for gfx950 behind a C-ABI (include/sanala.h);
+this package only loads that library and marshals torch tensors into it.
+"""
+from ._lib import EXPORTS, SanaError, library_path, load_library, status_string  # noqa: F401
+from .api import (  # noqa: F401
+    linear_attn,
+    qkv_linear_attn,
+    sana_linear_attn_fwd,
+    sana_qkv_linear_attn_fwd,
+)

@@ -1,0 +1,92 @@
+"""Python binding of libsanala: argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C-ABI (include/sanala.h).
+torch is used for device memory and the current stream; nothing here computes.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import SanaError
+
+_DTYPES = {torch.float32: _lib.SANA_F32, torch.bfloat16: _lib.SANA_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("libsanala takes device tensors")
+        if not t.is_contiguous():
+            raise ValueError("libsanala takes contiguous tensors")
+
+
+def sana_linear_attn_fwd(q, k, v, gq, gk, B: int, N: int, H: int, D: int, eps: float, out,
+                         stream=None, dtype: Optional[int] = None) -> None:
+    """Same arguments as the C entry point; tensors stand in for the device pointers."""
+    _check_dev(q, k, v, gq, gk, out)
+    if dtype is None:
+        dtype = _DTYPES[q.dtype]
+    lib = _lib.load_library()
+    st = lib.sana_linear_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gq), _ptr(gk), int(B), int(N), int(H), int(D),
+                                  float(eps), _ptr(out), _stream_handle(stream), int(dtype))
+    if st != _lib.SANA_OK:
+        raise SanaError(st, "sana_linear_attn_fwd")
+
+
+def sana_qkv_linear_attn_fwd(x, Wqkv, gq, gk, B: int, N: int, H: int, D: int, eps: float, out,
+                             stream=None) -> None:
+    _check_dev(x, Wqkv, gq, gk, out)
+    lib = _lib.load_library()
+    st = lib.sana_qkv_linear_attn_fwd(_ptr(x), _ptr(Wqkv), _ptr(gq), _ptr(gk), int(B), int(N), int(H), int(D),
+                                      float(eps), _ptr(out), _stream_handle(stream))
+    if st != _lib.SANA_OK:
+        raise SanaError(st, "sana_qkv_linear_attn_fwd")
+
+
+def linear_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gq: Optional[torch.Tensor],
+                gk: Optional[torch.Tensor], H: int, D: int = 32, eps: float = 1e-6,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """O = phi(Q) S / (phi(Q).z + eps) for q, k, v of shape [B, N, H*D] (fp32 or bf16)."""
+    if q.dim() != 3 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, N, H*D] shape")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be float32 or all bfloat16")
+    B, N, C = q.shape
+    if C != H * D:
+        raise ValueError(f"last dim {C} != H*D = {H}*{D}")
+    for g in (gq, gk):
+        if g is not None and (g.dtype != torch.float32 or g.numel() != C):
+            raise ValueError("gains must be float32 of length H*D")
+    if out is None:
+        out = torch.empty_like(q)
+    sana_linear_attn_fwd(q, k, v, gq, gk, B, N, H, D, eps, out)
+    return out
+
+
+def qkv_linear_attn(x: torch.Tensor, Wqkv: torch.Tensor, gq: Optional[torch.Tensor], gk: Optional[torch.Tensor],
+                    H: int, D: int = 32, eps: float = 1e-6, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x [B, N, C] bf16, Wqkv [C, 3C] bf16 -> linear attention of x @ Wqkv's q | k | v blocks."""
+    if x.dim() != 3 or x.dtype != torch.bfloat16 or Wqkv.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16 [B, N, C] and Wqkv bf16 [C, 3C]")
+    B, N, C = x.shape
+    if C != H * D or tuple(Wqkv.shape) != (C, 3 * C):
+        raise ValueError("shape mismatch between x, Wqkv and H*D")
+    if out is None:
+        out = torch.empty_like(x)
+    sana_qkv_linear_attn_fwd(x, Wqkv, gq, gk, B, N, H, D, eps, out)
+    return out

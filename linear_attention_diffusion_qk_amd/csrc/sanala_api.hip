@@ -1,0 +1,118 @@
+// C-ABI entry points of libsanala: argument checks, stream-ordered scratch, launches.
+#include "../../include/sanala.h"
+#include "attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_pool_once[kMaxDevices];
+
+// Keep freed stream-ordered scratch in the device's default pool instead of returning it to the
+// driver at every synchronisation, so steady-state calls do not allocate from the OS.
+void init_pool(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return;
+  std::call_once(g_pool_once[dev], [dev]() {
+    hipMemPool_t pool;
+    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+      uint64_t threshold = UINT64_MAX;
+      (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
+    }
+  });
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+sana_status_t check_common(int B, int N, int H, int D, float eps, const float* gq, const float* gk) {
+  if (B <= 0 || N <= 0 || H <= 0 || D <= 0) return SANA_ERR_INVALID_ARG;
+  if (!std::isfinite(eps) || eps < 0.f) return SANA_ERR_INVALID_ARG;
+  if ((gq == nullptr) != (gk == nullptr)) return SANA_ERR_INVALID_ARG;
+  if (D != sanala::kHeadDim) return SANA_ERR_UNSUPPORTED;
+  if (H > sanala::out_bf16_max_heads()) return SANA_ERR_UNSUPPORTED;
+  if (B > 65535) return SANA_ERR_UNSUPPORTED;
+  const double elems = (double)B * (double)N * (double)H * (double)D;
+  if (elems >= 1099511627776.0) return SANA_ERR_UNSUPPORTED;  // 2^40
+  if ((gq && !aligned16(gq)) || (gk && !aligned16(gk))) return SANA_ERR_MISALIGNED;
+  return SANA_OK;
+}
+
+}  // namespace
+
+extern "C" const char* sana_status_string(sana_status_t s) {
+  switch (s) {
+    case SANA_OK: return "ok";
+    case SANA_ERR_INVALID_ARG: return "invalid argument";
+    case SANA_ERR_UNSUPPORTED: return "unsupported shape or dtype (D must be 32, H <= 320, B <= 65535)";
+    case SANA_ERR_MISALIGNED: return "tensor pointer not 16-byte aligned";
+    case SANA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+extern "C" sana_status_t sana_linear_attn_fwd(const void* q, const void* k, const void* v, const float* gq,
+                                              const float* gk, int B, int N, int H, int D, float eps, void* out,
+                                              hipStream_t stream, sana_dtype_t dtype) {
+  if (!q || !k || !v || !out) return SANA_ERR_INVALID_ARG;
+  if (dtype != SANA_F32 && dtype != SANA_BF16) return SANA_ERR_INVALID_ARG;
+  sana_status_t st = check_common(B, N, H, D, eps, gq, gk);
+  if (st != SANA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SANA_ERR_MISALIGNED;
+  const size_t esz = dtype == SANA_BF16 ? 2 : 4;
+  const size_t tbytes = (size_t)B * N * H * D * esz;
+  if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, k, tbytes) || overlaps(out, tbytes, v, tbytes))
+    return SANA_ERR_INVALID_ARG;
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SANA_ERR_HIP;
+  init_pool(dev);
+  const bool norm = gq != nullptr;
+  const int dt = dtype == SANA_BF16 ? sanala::kDtypeBf16 : sanala::kDtypeF32;
+  const sanala::AttnPlan plan = sanala::plan_attn(B, N, H, dt, norm);
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, plan.ws_bytes, stream) != hipSuccess) return SANA_ERR_HIP;
+  const int64_t C = (int64_t)H * D;
+  hipError_t e = sanala::launch_attn(plan, q, C, k, v, C, gq, gk, eps, out, C, ws, stream);
+  const hipError_t ef = hipFreeAsync(ws, stream);
+  return (e == hipSuccess && ef == hipSuccess) ? SANA_OK : SANA_ERR_HIP;
+}
+
+extern "C" sana_status_t sana_qkv_linear_attn_fwd(const void* x, const void* Wqkv, const float* gq, const float* gk,
+                                                  int B, int N, int H, int D, float eps, void* out,
+                                                  hipStream_t stream) {
+  if (!x || !Wqkv || !out) return SANA_ERR_INVALID_ARG;
+  sana_status_t st = check_common(B, N, H, D, eps, gq, gk);
+  if (st != SANA_OK) return st;
+  if (!aligned16(x) || !aligned16(Wqkv) || !aligned16(out)) return SANA_ERR_MISALIGNED;
+  const int64_t C = (int64_t)H * D;
+  const int64_t M = (int64_t)B * N;
+  const size_t xbytes = (size_t)M * C * 2;
+  if (overlaps(out, xbytes, x, xbytes) || overlaps(out, xbytes, Wqkv, (size_t)C * 3 * C * 2))
+    return SANA_ERR_INVALID_ARG;
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SANA_ERR_HIP;
+  init_pool(dev);
+  const bool norm = gq != nullptr;
+  const sanala::AttnPlan plan = sanala::plan_attn(B, N, H, sanala::kDtypeBf16, norm);
+  const size_t qkv_bytes = ((size_t)M * 3 * C * 2 + 255) / 256 * 256;
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, qkv_bytes + plan.ws_bytes, stream) != hipSuccess) return SANA_ERR_HIP;
+  uint16_t* qkv = static_cast<uint16_t*>(ws);
+  hipError_t e = sanala::launch_qkv_gemm(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(Wqkv), qkv, M,
+                                         (int)C, stream);
+  if (e == hipSuccess)
+    e = sanala::launch_attn(plan, qkv, 3 * C, qkv + C, qkv + 2 * C, 3 * C, gq, gk, eps, out, C,
+                            static_cast<char*>(ws) + qkv_bytes, stream);
+  const hipError_t ef = hipFreeAsync(ws, stream);
+  return (e == hipSuccess && ef == hipSuccess) ? SANA_OK : SANA_ERR_HIP;
+}

@@ -1,0 +1,80 @@
+"""The C-ABI library loads without a GPU, exports every declared symbol, and rejects bad arguments on
+the host before any HIP call (no compute is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_diffusion_qk_amd as sanala
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "sanala.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sana_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared_symbols() == sorted(sanala.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sanala.load_library()
+    for name in _declared_symbols():
+        assert hasattr(lib, name), name
+    # the binding exposes the same names
+    for name in ("sana_linear_attn_fwd", "sana_qkv_linear_attn_fwd"):
+        assert callable(getattr(sanala, name))
+
+
+def test_status_strings():
+    for s in range(5):
+        assert sanala.status_string(s)
+    assert sanala.status_string(99) == "unknown status"
+
+
+# fake, 16-byte aligned "device" addresses: every call below must be rejected before it is used
+A, B_, C_, G1, G2, O = 0x1000, 0x2000000, 0x4000000, 0x6000000, 0x6001000, 0x8000000
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, B_, C_, G1, G2, 1, 8, 70, 32, 1e-6, O, 0, 1), 1),           # null q
+    ((A, B_, C_, G1, 0, 1, 8, 70, 32, 1e-6, O, 0, 1), 1),             # only one gain NULL
+    ((A, B_, C_, G1, G2, 0, 8, 70, 32, 1e-6, O, 0, 1), 1),            # B = 0
+    ((A, B_, C_, G1, G2, 1, -3, 70, 32, 1e-6, O, 0, 1), 1),           # N < 0
+    ((A, B_, C_, G1, G2, 1, 8, 70, 32, float("nan"), O, 0, 1), 1),    # eps NaN
+    ((A, B_, C_, G1, G2, 1, 8, 70, 32, -1.0, O, 0, 1), 1),            # eps < 0
+    ((A, B_, C_, G1, G2, 1, 8, 70, 32, 1e-6, O, 0, 7), 1),            # unknown dtype
+    ((A, B_, C_, G1, G2, 1, 8, 140, 16, 1e-6, O, 0, 1), 2),           # D != 32
+    ((A, B_, C_, G1, G2, 1, 8, 400, 32, 1e-6, O, 0, 1), 2),           # H too large
+    ((A, B_, C_, G1, G2, 70000, 8, 70, 32, 1e-6, O, 0, 1), 2),        # B too large
+    ((A + 2, B_, C_, G1, G2, 1, 8, 70, 32, 1e-6, O, 0, 1), 3),        # misaligned q
+    ((A, B_, C_, G1 + 4, G2, 1, 8, 70, 32, 1e-6, O, 0, 1), 3),        # misaligned gain
+    ((A, B_, C_, G1, G2, 1, 8, 70, 32, 1e-6, A + 16, 0, 1), 1),       # out overlaps q
+])
+def test_linear_attn_rejects(args, status):
+    lib = sanala.load_library()
+    assert lib.sana_linear_attn_fwd(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, B_, G1, G2, 1, 8, 70, 32, 1e-6, O, 0), 1),
+    ((A, B_, G1, 0, 1, 8, 70, 32, 1e-6, O, 0), 1),
+    ((A, B_, G1, G2, 1, 8, 70, 30, 1e-6, O, 0), 2),
+    ((A, B_ + 8, G1, G2, 1, 8, 70, 32, 1e-6, O, 0), 3),
+    ((A, B_, G1, G2, 1, 8, 70, 32, 1e-6, B_ + 64, 0), 1),            # out overlaps W
+])
+def test_qkv_rejects(args, status):
+    lib = sanala.load_library()
+    assert lib.sana_qkv_linear_attn_fwd(*args) == status
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    from linear_attention_diffusion_qk_amd import _lib
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        _lib.load_library()
