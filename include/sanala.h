@@ -92,6 +92,22 @@ sana_status_t sana_qkv_linear_attn_fwd(const void* x, const void* Wqkv,
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* sana_status_string(sana_status_t status);
 
+/*
+ * Measurement support for benchmarks and profilers (not part of the method).
+ *
+ * sana_timing_enable(1) makes every later call from the calling host thread record a HIP event pair
+ * on its stream around each kernel it launches; sana_timing_enable(0) stops it.  Events are created
+ * once per thread and reused.  Recording adds a little host and queue overhead, so throughput runs
+ * leave timing off.
+ *
+ * sana_timing_last waits for the events of the most recent call on this thread and writes, for up
+ * to `capacity` kernels in launch order, a static kernel name (names may be NULL) and the kernel's
+ * duration in milliseconds (ms may be NULL; -1 if an event failed).  Returns the number of kernels
+ * that call launched.
+ */
+sana_status_t sana_timing_enable(int enable);
+int sana_timing_last(const char** names, float* ms, int capacity);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,4 +9,6 @@ from .api import (  # noqa: F401
     qkv_linear_attn,
     sana_linear_attn_fwd,
     sana_qkv_linear_attn_fwd,
+    sana_timing_enable,
+    sana_timing_last,
 )

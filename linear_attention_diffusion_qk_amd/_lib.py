@@ -20,7 +20,8 @@ SANA_F32 = 0
 SANA_BF16 = 1
 
 # Every symbol include/sanala.h declares.
-EXPORTS = ("sana_linear_attn_fwd", "sana_qkv_linear_attn_fwd", "sana_status_string")
+EXPORTS = ("sana_linear_attn_fwd", "sana_qkv_linear_attn_fwd", "sana_status_string",
+           "sana_timing_enable", "sana_timing_last")
 
 _lock = threading.Lock()
 _lib = None
@@ -48,6 +49,10 @@ def load_library() -> ctypes.CDLL:
         lib.sana_qkv_linear_attn_fwd.restype = ci
         lib.sana_status_string.argtypes = [ci]
         lib.sana_status_string.restype = ctypes.c_char_p
+        lib.sana_timing_enable.argtypes = [ci]
+        lib.sana_timing_enable.restype = ci
+        lib.sana_timing_last.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), ci]
+        lib.sana_timing_last.restype = ci
         _lib = lib
         return lib
 

@@ -90,3 +90,18 @@ def qkv_linear_attn(x: torch.Tensor, Wqkv: torch.Tensor, gq: Optional[torch.Tens
         out = torch.empty_like(x)
     sana_qkv_linear_attn_fwd(x, Wqkv, gq, gk, B, N, H, D, eps, out)
     return out
+
+
+def sana_timing_enable(enable: bool) -> None:
+    """Record a HIP event pair around every kernel of later calls from this thread (measurement only)."""
+    _lib.load_library().sana_timing_enable(1 if enable else 0)
+
+
+def sana_timing_last(capacity: int = 32):
+    """[(kernel name, ms)] of the most recent call on this thread, in launch order (waits for it)."""
+    import ctypes
+    lib = _lib.load_library()
+    names = (ctypes.c_char_p * capacity)()
+    ms = (ctypes.c_float * capacity)()
+    n = lib.sana_timing_last(names, ms, capacity)
+    return [(names[i].decode(), float(ms[i])) for i in range(min(n, capacity))]

@@ -1,4 +1,4 @@
-// Internal host interface between the C-ABI entry points and the attention kernels.
+// Internal host interface between the C-ABI entry points and the kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,8 +16,10 @@ constexpr int kDtypeBf16 = 1;
 struct AttnPlan {
   int B, N, H, dtype;
   bool norm;
-  int Tc;  // tokens per KV chunk (multiple of 64)
-  int NC;  // number of chunks per sample
+  int Tc;               // tokens per KV chunk (multiple of 64)
+  int NC;               // number of chunks per sample
+  bool out_persistent;  // bf16 output through the persistent LDS-resident-state kernel
+  int num_cus;          // compute units of the current device
   size_t off_rk, off_rq, off_part, off_S32, off_z, off_Sop;
   size_t ws_bytes;
 };
@@ -29,9 +31,30 @@ hipError_t launch_attn(const AttnPlan& p, const void* q, int64_t ldq, const void
                        const float* gq, const float* gk, float eps, void* out, int64_t ldo, void* ws,
                        hipStream_t stream);
 
-int out_bf16_max_heads();
+hipError_t launch_attn_f32(const AttnPlan& p, const float* q, int64_t ldq, const float* k, const float* v,
+                           int64_t ldkv, const float* gq, const float* gk, float eps, float* out, int64_t ldo,
+                           void* ws, hipStream_t stream);
+hipError_t launch_attn_bf16(const AttnPlan& p, const uint16_t* q, int64_t ldq, const uint16_t* k, const uint16_t* v,
+                            int64_t ldkv, const float* gq, const float* gk, float eps, uint16_t* out, int64_t ldo,
+                            void* ws, int num_cus, hipStream_t stream);
+size_t out_persist_lds_bytes(int H);
+size_t bf16_operand_bytes(int64_t BH);
+
+int max_heads();
 
 // qkv[M, 3C] = x[M, C] @ w[C, 3C], bf16 in / bf16 out (fp32 accumulation).
 hipError_t launch_qkv_gemm(const uint16_t* x, const uint16_t* w, uint16_t* qkv, int64_t M, int C, hipStream_t stream);
+
+// Measurement hooks (no-ops unless timing is enabled on the calling host thread): an event pair is
+// recorded on `s` around each kernel launch.
+void timing_begin(const char* name, hipStream_t s);
+void timing_end(hipStream_t s);
+
+#define SANA_LAUNCH(name, ...)  \
+  do {                          \
+    timing_begin(name, stream); \
+    __VA_ARGS__;                \
+    timing_end(stream);         \
+  } while (0)
 
 }  // namespace sanala

@@ -1,0 +1,551 @@
+// bf16-storage path of the linear attention on gfx950 (fp32 accumulation, bf16 MFMA operands).
+//
+// "Sana: Efficient High-Resolution Image Synthesis with Linear Diffusion Transformers" (paper notes),
+// section 2.1, Eq. (1), per head, in the precompute-then-apply order the notes give after Eq. (1);
+// phi(x) = ReLU(x * r * g), r = 1/sqrt(mean_c x_c^2 + eps) over all channels of a token ("SANA 1.5:
+// Efficient Scaling of Training-Time and Inference-Time Compute in Linear Diffusion Transformer"
+// (research notes), model architecture, QK Norm).
+//
+// Algebra used to keep per-element work small (exact up to rounding):
+//   r > 0, so ReLU(x * r * g) = r * |g| * ReLU(s * x) with s = sign(g); ReLU(s * x) of a bf16 x is
+//   exact in bf16 (a sign flip and a packed integer max).  Hence, with G_d = |gq_d| * |gk_d|,
+//     S[d][e] * |gq_d| = G_d * sum_j r_k,j ReLU(sk_d k_j,d) v_j,e         (S' below)
+//     z[d] * |gq_d|    = G_d * sum_j r_k,j ReLU(sk_d k_j,d)                (z' below)
+//     O_i[e] = r_q,i a / (r_q,i b + eps) = a / (b + eps / r_q,i),
+//   a = sum_d ReLU(sq_d q_i,d) S'[d][e],  b = sum_d ReLU(sq_d q_i,d) z'[d].
+//   The query side therefore needs no fp32 multiply per element, and r_q enters once per token.
+//
+// Launches on one stream:
+//   rowstats  r_k for every K row (one wave per 2240-channel row)
+//   kv_state  per (b, head pair, token chunk): S~ = sum_j (r_k,j ReLU(sk k_j)) v_j^T and
+//             z~ = sum_j r_k,j ReLU(sk k_j) on v_mfma_f32_32x32x16_bf16 (phi(K) rounded to bf16 once,
+//             fp32 accumulation; z~ from a second MFMA against a ones operand)
+//   kv_reduce sums the chunk partials in chunk order (deterministic, no float atomics) and writes
+//             S' as bf16 A operands of v_mfma_f32_16x16x32_bf16 and z' as a bf16 hi + lo pair
+//             (skipped when one chunk covers the sequence: kv_state then writes them itself)
+//   out       persistent blocks hold S', z' and the query sign masks of the current sample in LDS
+//             and stream 16-token tiles of Q (the next tile's loads in flight): r_q from the Q rows
+//             held in registers (v_dot2_f32_bf16), a on MFMA, b by v_dot2_f32_bf16.
+#include "rowstats.h"
+
+#include <algorithm>
+
+namespace sanala {
+
+constexpr int kOpPerHead = 2 * 64 * 8;  // S' operand per head: 2 e-blocks x 64 lanes x 8 bf16
+constexpr int kZopPerHead = 2 * kHeadDim;  // z' per head: 32 bf16 hi, then 32 bf16 lo
+constexpr int kSgnPerHead = 16;            // query sign masks per head: 4 lane groups x 4 words
+
+// Position of S'[d][e] inside a head's operand block.  Lane l = m + 16*kg of e-block eb holds
+// S'[8*kg + j][e] (j = 0..7) with e = 8*(m/4) + 4*eb + m%4; with that column order the MFMA result
+// lane (t, kg) receives output channels 8kg..8kg+7 of token t.
+__device__ __forceinline__ int sop_index(int d, int e) {
+  const int m = 4 * (e >> 3) + (e & 3), eb = (e >> 2) & 1, kg = d >> 3, j = d & 7;
+  return eb * 512 + (m + 16 * kg) * 8 + j;
+}
+
+// Writes one reduced state element (i < 1024: S~[i/32][i%32]; else z~[i-1024]) of head h of sample
+// row bh as the output kernel's operands, scaled by G_d = |gq_d| |gk_d| (1 without the norm).
+template <bool NORM>
+__device__ __forceinline__ void emit_state(int64_t bh, int h, int i, float s, const float* __restrict__ gq,
+                                           const float* __restrict__ gk, uint16_t* __restrict__ Sop,
+                                           uint16_t* __restrict__ zop) {
+  const int d = i < kHeadDim * kHeadDim ? i / kHeadDim : i - kHeadDim * kHeadDim;
+  if (NORM) s *= fabsf(gq[h * kHeadDim + d]) * fabsf(gk[h * kHeadDim + d]);
+  if (i < kHeadDim * kHeadDim) {
+    Sop[bh * kOpPerHead + sop_index(d, i % kHeadDim)] = (uint16_t)f32_to_bf16_bits(s);
+  } else {
+    const uint32_t hi = f32_to_bf16_bits(s);
+    zop[bh * kZopPerHead + d] = (uint16_t)hi;
+    zop[bh * kZopPerHead + kHeadDim + d] = (uint16_t)f32_to_bf16_bits(s - __uint_as_float(hi << 16));
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// KV state.  Block = 4 waves; block (c, p, b) owns heads 2p, 2p+1 and tokens [c*Tc, min(N, c*Tc+Tc)),
+// staged through LDS in 64-token sub-blocks; the next sub-block's global loads are in flight while
+// the current one is multiplied.  Wave w: head 2p + (w & 1), token half (w >> 1) of each sub-block.
+// MFMA 32x32x16: A[d][t] = bf16(r_t ReLU(s_d k_t,d)) (lane d + 32g holds tokens 8g..8g+7 of the
+// 16-token step), B[t][e] = v_t,e; accumulator lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4,
+// column l%32.  A second MFMA against an all-ones B gives z~ in every column.
+// ---------------------------------------------------------------------------------------------
+template <bool NORM>
+__global__ __launch_bounds__(256) void kv_state_bf16(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                     int64_t ld, const float* __restrict__ r_k,
+                                                     const float* __restrict__ gq, const float* __restrict__ gk,
+                                                     int N, int H, int Tc, int NC, float* __restrict__ part,
+                                                     uint16_t* __restrict__ Sop, uint16_t* __restrict__ zop) {
+  constexpr int SB = 64;     // tokens per sub-block
+  constexpr int PITCH = 72;  // bf16 per staged row (64 used)
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[SB * PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[SB * PITCH];
+  __shared__ __attribute__((aligned(16))) float rs[SB];
+  __shared__ float fin[2 * kPartStride];  // wave hand-over, then the block's state of the head pair
+
+  const int c = blockIdx.x, p = blockIdx.y, b = blockIdx.z;
+  const int h0 = 2 * p;
+  const int nh = min(2, H - h0);
+  const int n_begin = c * Tc;
+  const int n_end = min(N, n_begin + Tc);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int hh = w & 1, th = w >> 1;
+  const int d = lane & 31, grp = lane >> 5;
+  const int hcol = min(h0 + hh, H - 1) * kHeadDim + d;
+  const uint32_t sgn = (NORM && gk[hcol] < 0.f) ? 0x80008000u : 0u;  // flips both tokens of a pair
+  const int64_t row0 = (int64_t)b * N;
+  const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+
+  u32x4 pk[2], pv[2];
+  float pr = 1.f;
+  auto gload = [&](int n0) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int i = tid + it * 256;
+      const int row = i >> 3, cu = i & 7;  // cu: 16-byte unit of the 128-byte head pair
+      const int n = n0 + row;
+      pk[it] = u32x4{0u, 0u, 0u, 0u};
+      pv[it] = u32x4{0u, 0u, 0u, 0u};
+      if (n < n_end && (cu >> 2) < nh) {
+        const int64_t off = (row0 + n) * ld + h0 * kHeadDim + cu * 8;
+        pk[it] = load16(k + off);
+        pv[it] = load16(v + off);
+      }
+    }
+    if (tid < SB) pr = (NORM && n0 + tid < n_end) ? r_k[row0 + n0 + tid] : 1.0f;  // rows past the end are zero
+  };
+
+  f32x16 acc, accz;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    acc[r] = 0.f;
+    accz[r] = 0.f;
+  }
+
+  if (n_begin < n_end) gload(n_begin);
+  for (int n0 = n_begin; n0 < n_end; n0 += SB) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int i = tid + it * 256;
+      const int row = i >> 3, cu = i & 7;
+      store16(&Ks[row * PITCH + cu * 8], pk[it]);
+      store16(&Vs[row * PITCH + cu * 8], pv[it]);
+    }
+    if (tid < SB) rs[tid] = pr;
+    __syncthreads();
+    if (n0 + SB < n_end) gload(n0 + SB);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int tb = 32 * th + 16 * s + 8 * grp;  // this lane's tokens tb .. tb+7
+      const int col = hh * kHeadDim + d;
+      uint32_t aw[4], bw[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t0 = tb + 2 * u;
+        const uint32_t kp = (uint32_t)Ks[t0 * PITCH + col] | ((uint32_t)Ks[(t0 + 1) * PITCH + col] << 16);
+        bw[u] = (uint32_t)Vs[t0 * PITCH + col] | ((uint32_t)Vs[(t0 + 1) * PITCH + col] << 16);
+        aw[u] = relu_bf16x2(kp ^ sgn);
+      }
+      if (NORM) {
+        const f32x4 r0 = *reinterpret_cast<const f32x4*>(&rs[tb]);
+        const f32x4 r1 = *reinterpret_cast<const f32x4*>(&rs[tb + 4]);
+        const float rr[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          aw[u] = cvt_pk_bf16(bf16_lo(aw[u]) * rr[2 * u], bf16_hi(aw[u]) * rr[2 * u + 1]);
+      }
+      const bf16x8 A = as_bf16x8(u32x4{aw[0], aw[1], aw[2], aw[3]});
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, as_bf16x8(u32x4{bw[0], bw[1], bw[2], bw[3]}), acc, 0, 0, 0);
+      accz = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, as_bf16x8(ones), accz, 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // Combine the two token halves of each head in a fixed order (wave hh + 2 hands over to wave hh),
+  // leaving the block's state of head hh as S~[d][e] and z~[d] in `fin`.
+  float* fh = fin + hh * kPartStride;
+  if (th == 1) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * grp + (r & 3);
+      fh[row * kHeadDim + d] = acc[r];
+      if (d == 0) fh[kHeadDim * kHeadDim + row] = accz[r];
+    }
+  }
+  __syncthreads();
+  if (th == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * grp + (r & 3);
+      fh[row * kHeadDim + d] = acc[r] + fh[row * kHeadDim + d];
+      if (d == 0) fh[kHeadDim * kHeadDim + row] = accz[r] + fh[kHeadDim * kHeadDim + row];
+    }
+  }
+  __syncthreads();
+  const int64_t bh0 = (int64_t)b * H + h0;
+  if (NC == 1) {
+    for (int i = tid; i < nh * kPartStride; i += 256) {
+      const int hl = i / kPartStride, off = i - hl * kPartStride;
+      emit_state<NORM>(bh0 + hl, h0 + hl, off, fin[i], gq, gk, Sop, zop);
+    }
+    return;
+  }
+  for (int i = tid; i < nh * kPartStride; i += 256) {
+    const int hl = i / kPartStride, off = i - hl * kPartStride;
+    part[((bh0 + hl) * NC + c) * kPartStride + off] = fin[i];
+  }
+}
+
+// One thread per state element (b, h, i): sum of the chunk partials in chunk order (8 loads in flight
+// per step), then the output kernel's operands.
+template <bool NORM>
+__global__ __launch_bounds__(256) void kv_reduce_bf16(const float* __restrict__ part, int NC, int H, int64_t BH,
+                                                      const float* __restrict__ gq, const float* __restrict__ gk,
+                                                      uint16_t* __restrict__ Sop, uint16_t* __restrict__ zop) {
+  const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gi >= BH * kPartStride) return;
+  const int64_t bh = gi / kPartStride;
+  const int i = (int)(gi - bh * kPartStride);
+  const float* src = part + bh * NC * kPartStride + i;
+  float s = 0.f;
+  int c = 0;
+  for (; c + 8 <= NC; c += 8) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = src[(int64_t)(c + u) * kPartStride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += x[u];
+  }
+  for (; c < NC; ++c) s += src[(int64_t)c * kPartStride];
+  emit_state<NORM>(bh, (int)(bh % H), i, s, gq, gk, Sop, zop);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Per-head output math shared by both output kernels.  qv: lane l = t + 16*kg holds query dims
+// 8kg..8kg+7 of token t (bf16 pairs); sg: the sign masks of those dims; a0/a1: the two e-blocks of
+// S'^T; zh/zl: z' hi and lo at those dims; epsr = eps / r_q of token t; even_row: lane index even.
+// Returns output channels 8kg..8kg+7 of token t as bf16 (1/den by v_rcp_f32, 1 ulp).
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 head_out(u32x4 qv, u32x4 sg, bf16x8 a0, bf16x8 a1, u32x4 zh, u32x4 zl, float epsr,
+                                          bool even_row) {
+  u32x4 psi;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) psi[u] = relu_bf16x2(qv[u] ^ sg[u]);
+  const bf16x8 Bq = as_bf16x8(psi);
+  // z-block of S'^T: rows with even index hold z' hi, odd rows z' lo, so result registers 0 and 1 of
+  // every lane are psi.z'_hi and psi.z'_lo of its token, and their sum is the denominator.
+  const u32x4 zsel = {even_row ? zh[0] : zl[0], even_row ? zh[1] : zl[1], even_row ? zh[2] : zl[2],
+                      even_row ? zh[3] : zl[3]};
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f}, oz = {0.f, 0.f, 0.f, 0.f};
+  o0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, Bq, o0, 0, 0, 0);
+  o1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, Bq, o1, 0, 0, 0);
+  oz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(zsel), Bq, oz, 0, 0, 0);
+  const float inv = __builtin_amdgcn_rcpf((oz[0] + oz[1]) + epsr);
+  return u32x4{cvt_pk_bf16(o0[0] * inv, o0[1] * inv), cvt_pk_bf16(o0[2] * inv, o0[3] * inv),
+               cvt_pk_bf16(o1[0] * inv, o1[1] * inv), cvt_pk_bf16(o1[2] * inv, o1[3] * inv)};
+}
+
+// Sign masks (0x8000 per negative gain) of query dims 8kg + 2u, 8kg + 2u + 1 of head h.
+template <bool NORM>
+__device__ __forceinline__ uint32_t sign_word(const float* __restrict__ gq, int h, int kg, int u) {
+  if (!NORM) return 0u;
+  const int d0 = h * kHeadDim + 8 * kg + 2 * u;
+  return (gq[d0] < 0.f ? 0x8000u : 0u) | (gq[d0 + 1] < 0.f ? 0x80000000u : 0u);
+}
+
+// Lane swap between the two 8-lane halves of every 16-lane row (DPP row_ror:8): lanes whose bank
+// (4-lane group within the row) is enabled in `banks` take `src` from the lane 8 away; the others
+// keep `old`.
+template <int BANKS>
+__device__ __forceinline__ u32x4 swap_halves(u32x4 old, u32x4 src) {
+  u32x4 r;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    r[u] = (uint32_t)__builtin_amdgcn_update_dpp((int)old[u], (int)src[u], 0x128 /* row_ror:8 */, 0xf, BANKS, false);
+  return r;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Persistent output kernel.  One block per CU keeps S', z' and the query sign masks of the current
+// sample in LDS and walks a contiguous run of 16-token tiles.  Wave w owns head pairs
+// [w*PPW, w*PPW + PPW).  A head pair of one token is one 128-byte span of the Q or O row, so every
+// load and store instruction touches 8 whole rows x 128 bytes: load j of a pair gives lane
+// (n = l%16, kg = l/16) the 16 bytes (token 8j + n%8, head 2p + n/8, dims 8kg..8kg+7), and one DPP
+// swap of the row halves turns the two loads into the MFMA B operands of the two heads
+// (lane (n, kg) = token n, dims 8kg..8kg+7); stores use the inverse swap.  Q tiles alternate
+// between two register sets: each step first issues the loads of the next tile (unconditionally,
+// clamped to the last tile, so the wait for the current tile leaves them in flight) and then
+// consumes the current one; nothing else in the tile loop reads global memory.  The row sums of
+// squares are combined across waves through LDS in a fixed order.
+// ---------------------------------------------------------------------------------------------
+template <int PPW, bool NORM>
+__global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restrict__ q, int64_t ldq,
+                                                        const float* __restrict__ gq, const uint16_t* __restrict__ Sop,
+                                                        const uint16_t* __restrict__ zop, int B, int N, int H, float eps,
+                                                        float inv_C, uint16_t* __restrict__ out, int64_t ldo,
+                                                        int tiles_per_block) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  uint16_t* Ss = reinterpret_cast<uint16_t*>(smem);                          // [H][kOpPerHead]
+  uint16_t* Zs = Ss + (size_t)H * kOpPerHead;                                // [H][kZopPerHead]
+  uint32_t* Gs = reinterpret_cast<uint32_t*>(Zs + (size_t)H * kZopPerHead);  // [H][kSgnPerHead]
+  float* ssq = reinterpret_cast<float*>(Gs + (size_t)H * kSgnPerHead);       // [2][8 waves][16]
+
+  const int NW = blockDim.x >> 6;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int n16 = lane & 15, kg = lane >> 4;
+  const int tok8 = n16 & 7, hsel = n16 >> 3;  // load/store role of this lane within a head pair
+  const int tiles_per_sample = (N + 15) / 16;
+  const int64_t total = (int64_t)B * tiles_per_sample;
+  const int64_t tau0 = (int64_t)blockIdx.x * tiles_per_block;
+  const int64_t tau_end = min(total, tau0 + tiles_per_block);
+  if (tau0 >= tau_end) return;
+
+  for (int i = tid; i < H * kSgnPerHead; i += NW * 64)
+    Gs[i] = sign_word<NORM>(gq, i / kSgnPerHead, (i / 4) & 3, i & 3);
+
+  // Raw loads of one tile: qr[2*i + j] = load j of pair w*PPW + i.  Addresses are clamped into the
+  // tensor; lanes past N or H are never stored.
+  auto load_tile = [&](int64_t tau, u32x4* qr) {
+    tau = min(tau, tau_end - 1);
+    const int64_t bb = tau / tiles_per_sample;
+    const int n0 = (int)(tau - bb * tiles_per_sample) * 16;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint16_t* row = q + (bb * N + min(n0 + 8 * j + tok8, N - 1)) * ldq + kg * 8;
+#pragma unroll
+      for (int i = 0; i < PPW; ++i)
+        qr[2 * i + j] = load16(row + min(2 * (w * PPW + i) + hsel, H - 1) * kHeadDim);
+    }
+  };
+
+  int64_t cur_b = -1;
+  auto step = [&](int64_t tau, u32x4* cur, u32x4* nxt) {
+    const int64_t bb = tau / tiles_per_sample;
+    const int n0 = (int)(tau - bb * tiles_per_sample) * 16;
+    if (bb != cur_b) {  // uniform across the block
+      __syncthreads();
+      const u32x4* s1 = reinterpret_cast<const u32x4*>(Sop + bb * H * kOpPerHead);
+      u32x4* d1 = reinterpret_cast<u32x4*>(Ss);
+      const int n1 = H * kOpPerHead / 8;
+      for (int i0 = tid; i0 < n1; i0 += 8 * NW * 64) {
+        u32x4 tmp[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) tmp[u] = s1[min(i0 + u * NW * 64, n1 - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (i0 + u * NW * 64 < n1) d1[i0 + u * NW * 64] = tmp[u];
+      }
+      const u32x4* s2 = reinterpret_cast<const u32x4*>(zop + bb * H * kZopPerHead);
+      u32x4* d2 = reinterpret_cast<u32x4*>(Zs);
+      for (int i = tid; i < H * kZopPerHead / 8; i += NW * 64) d2[i] = s2[i];
+      __syncthreads();
+      cur_b = bb;
+    }
+    load_tile(tau + 1, nxt);
+    // MFMA operand layout: lane (n16, kg) = token n16 of the tile, dims 8kg..8kg+7.
+    u32x4 bq[2 * PPW];
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+      bq[2 * i] = swap_halves<0xc>(cur[2 * i], cur[2 * i + 1]);
+      bq[2 * i + 1] = swap_halves<0x3>(cur[2 * i + 1], cur[2 * i]);
+    }
+    float epsr = eps;
+    if (NORM) {
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < 2 * PPW; ++i)
+        if (2 * w * PPW + i < H) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) ss = dot2_bf16(bq[i][u], bq[i][u], ss);
+        }
+      ss = sum_over_lane_groups(ss);
+      float* sb = ssq + (tau & 1) * 8 * 16;
+      if (kg == 0) sb[w * 16 + n16] = ss;
+      __syncthreads();
+      float tot = 0.f;
+      for (int ww = 0; ww < NW; ++ww) tot += sb[ww * 16 + n16];
+      epsr = eps * sqrtf(tot * inv_C + eps);  // eps / r_q
+    }
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+      const int h0 = 2 * (w * PPW + i);
+      if (h0 < H) {
+        u32x4 o[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int h = min(h0 + j, H - 1);
+          const uint16_t* sh = Ss + h * kOpPerHead + lane * 8;
+          const uint16_t* zh = Zs + h * kZopPerHead + kg * 8;
+          o[j] = head_out(bq[2 * i + j], *reinterpret_cast<const u32x4*>(Gs + h * kSgnPerHead + kg * 4),
+                          as_bf16x8(*reinterpret_cast<const u32x4*>(sh)),
+                          as_bf16x8(*reinterpret_cast<const u32x4*>(sh + 512)), *reinterpret_cast<const u32x4*>(zh),
+                          *reinterpret_cast<const u32x4*>(zh + kHeadDim), epsr, (lane & 1) == 0);
+        }
+        const u32x4 st[2] = {swap_halves<0xc>(o[0], o[1]), swap_halves<0x3>(o[1], o[0])};
+        const int h = h0 + hsel;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = n0 + 8 * j + tok8;
+          if (n < N && h < H) store16(out + (bb * N + n) * ldo + h * kHeadDim + kg * 8, st[j]);
+        }
+      }
+    }
+  };
+
+  u32x4 qa[2 * PPW], qb[2 * PPW];
+  load_tile(tau0, qa);
+  for (int64_t tau = tau0; tau < tau_end; tau += 2) {
+    step(tau, qa, qb);
+    if (tau + 1 < tau_end) step(tau + 1, qb, qa);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Non-persistent output kernel (few tiles, or H too large for the LDS-resident state).  Block =
+// 4 waves over 16 tokens of sample b and up to 4*HPW heads (blockIdx.z); wave w owns heads
+// [g0 + w*HPW, g0 + w*HPW + HPW).  PRE_R = false: the block covers all H heads and forms r_q from the
+// Q rows it holds; PRE_R = true: r_q comes from a row-statistics pass (H > 4*HPW).
+// ---------------------------------------------------------------------------------------------
+template <int HPW, bool NORM, bool PRE_R>
+__global__ __launch_bounds__(256) void out_bf16(const uint16_t* __restrict__ q, int64_t ldq,
+                                                const float* __restrict__ gq, const uint16_t* __restrict__ Sop,
+                                                const uint16_t* __restrict__ zop, const float* __restrict__ r_q, int N,
+                                                int H, float eps, float inv_C, uint16_t* __restrict__ out,
+                                                int64_t ldo) {
+  __shared__ float ssq[4][16];
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int t = lane & 15, kg = lane >> 4;
+  const int n = blockIdx.x * 16 + t;
+  const int hbeg = blockIdx.z * 4 * HPW + w * HPW;
+  const int hcnt = max(0, min(HPW, H - hbeg));
+  const int64_t row0 = (int64_t)b * N;
+  const uint16_t* row = q + (row0 + min(n, N - 1)) * ldq + kg * 8;
+
+  u32x4 qr[HPW];
+#pragma unroll
+  for (int i = 0; i < HPW; ++i) qr[i] = load16(row + min(hbeg + i, H - 1) * kHeadDim);
+  float epsr = eps;
+  if (NORM && PRE_R) {
+    epsr = eps / r_q[row0 + min(n, N - 1)];
+  } else if (NORM) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < HPW; ++i)
+      if (i < hcnt) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ss = dot2_bf16(qr[i][u], qr[i][u], ss);
+      }
+    ss = sum_over_lane_groups(ss);
+    if (kg == 0) ssq[w][t] = ss;
+    __syncthreads();
+    const float tot = ((ssq[0][t] + ssq[1][t]) + ssq[2][t]) + ssq[3][t];
+    epsr = eps * sqrtf(tot * inv_C + eps);
+  }
+#pragma unroll
+  for (int i = 0; i < HPW; ++i) {
+    if (i < hcnt) {
+      const int h = hbeg + i;
+      const int64_t bh = (int64_t)b * H + h;
+      const u32x4 sg = {sign_word<NORM>(gq, h, kg, 0), sign_word<NORM>(gq, h, kg, 1), sign_word<NORM>(gq, h, kg, 2),
+                        sign_word<NORM>(gq, h, kg, 3)};
+      const uint16_t* sh = Sop + bh * kOpPerHead + lane * 8;
+      const uint16_t* zh = zop + bh * kZopPerHead + kg * 8;
+      const u32x4 o = head_out(qr[i], sg, as_bf16x8(load16(sh)), as_bf16x8(load16(sh + 512)), load16(zh),
+                               load16(zh + kHeadDim), epsr, (lane & 1) == 0);
+      if (n < N) store16(out + (row0 + n) * ldo + h * kHeadDim + kg * 8, o);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Host launch of the bf16 path.
+// ---------------------------------------------------------------------------------------------
+
+size_t out_persist_lds_bytes(int H) {
+  return (size_t)H * (kOpPerHead * 2 + kZopPerHead * 2 + kSgnPerHead * 4) + 2 * 8 * 16 * 4;
+}
+
+size_t bf16_operand_bytes(int64_t BH) { return (size_t)BH * (kOpPerHead + kZopPerHead) * 2; }
+
+constexpr int kPersistPPW = 5;  // head pairs per wave in the persistent output kernel (<= 8 waves: H <= 80)
+
+hipError_t launch_attn_bf16(const AttnPlan& p, const uint16_t* q, int64_t ldq, const uint16_t* k, const uint16_t* v,
+                            int64_t ldkv, const float* gq, const float* gk, float eps, uint16_t* out, int64_t ldo,
+                            void* ws, int num_cus, hipStream_t stream) {
+  char* base = static_cast<char*>(ws);
+  float* r_k = reinterpret_cast<float*>(base + p.off_rk);
+  float* part = reinterpret_cast<float*>(base + p.off_part);
+  uint16_t* Sop = reinterpret_cast<uint16_t*>(base + p.off_Sop);
+  uint16_t* zop = Sop + (size_t)p.B * p.H * kOpPerHead;
+  const int B = p.B, N = p.N, H = p.H, C = H * kHeadDim;
+  const int64_t rows = (int64_t)B * N;
+  const int64_t BH = (int64_t)B * H;
+  const unsigned rs_blocks = (unsigned)((rows + 3) / 4);
+
+  if (p.norm)
+    SANA_LAUNCH("rowstats_k", rowstats_kernel<uint16_t><<<rs_blocks, 256, 0, stream>>>(k, ldkv, rows, C, eps, r_k));
+  const dim3 grid(p.NC, (H + 1) / 2, B);
+  if (p.norm)
+    SANA_LAUNCH("kv_state", kv_state_bf16<true><<<grid, 256, 0, stream>>>(k, v, ldkv, r_k, gq, gk, N, H, p.Tc, p.NC,
+                                                                          part, Sop, zop));
+  else
+    SANA_LAUNCH("kv_state", kv_state_bf16<false><<<grid, 256, 0, stream>>>(k, v, ldkv, nullptr, nullptr, nullptr, N, H,
+                                                                           p.Tc, p.NC, part, Sop, zop));
+  if (p.NC > 1) {
+    const unsigned blocks = (unsigned)((BH * kPartStride + 255) / 256);
+    if (p.norm)
+      SANA_LAUNCH("kv_reduce", kv_reduce_bf16<true><<<blocks, 256, 0, stream>>>(part, p.NC, H, BH, gq, gk, Sop, zop));
+    else
+      SANA_LAUNCH("kv_reduce",
+                  kv_reduce_bf16<false><<<blocks, 256, 0, stream>>>(part, p.NC, H, BH, nullptr, nullptr, Sop, zop));
+  }
+
+  const float inv_C = 1.0f / (float)C;
+  if (p.out_persistent) {
+    const int64_t tiles = (int64_t)B * ((N + 15) / 16);
+    const int blocks = (int)std::min<int64_t>(num_cus, tiles);
+    const int per = (int)((tiles + blocks - 1) / blocks);
+    const int nblk = (int)((tiles + per - 1) / per);
+    const size_t lds = out_persist_lds_bytes(H);
+    const int nw = ((H + 1) / 2 + kPersistPPW - 1) / kPersistPPW;
+    static bool attr_set = false;
+    if (!attr_set) {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&out_persist_bf16<kPersistPPW, true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&out_persist_bf16<kPersistPPW, false>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      attr_set = true;
+    }
+    if (p.norm)
+      SANA_LAUNCH("out", out_persist_bf16<kPersistPPW, true><<<nblk, nw * 64, lds, stream>>>(
+                             q, ldq, gq, Sop, zop, B, N, H, eps, inv_C, out, ldo, per));
+    else
+      SANA_LAUNCH("out", out_persist_bf16<kPersistPPW, false><<<nblk, nw * 64, lds, stream>>>(
+                             q, ldq, nullptr, Sop, zop, B, N, H, eps, inv_C, out, ldo, per));
+    return hipGetLastError();
+  }
+  constexpr int HPW = 18;
+  if (H <= 4 * HPW) {
+    const dim3 ogrid((N + 15) / 16, B, 1);
+    if (p.norm)
+      SANA_LAUNCH("out", out_bf16<HPW, true, false><<<ogrid, 256, 0, stream>>>(q, ldq, gq, Sop, zop, nullptr, N, H, eps,
+                                                                              inv_C, out, ldo));
+    else
+      SANA_LAUNCH("out", out_bf16<HPW, false, false><<<ogrid, 256, 0, stream>>>(q, ldq, nullptr, Sop, zop, nullptr, N, H,
+                                                                               eps, inv_C, out, ldo));
+  } else {
+    const dim3 ogrid((N + 15) / 16, B, (H + 4 * HPW - 1) / (4 * HPW));
+    float* r_q = reinterpret_cast<float*>(base + p.off_rq);
+    if (p.norm) {
+      SANA_LAUNCH("rowstats_q", rowstats_kernel<uint16_t><<<rs_blocks, 256, 0, stream>>>(q, ldq, rows, C, eps, r_q));
+      SANA_LAUNCH("out", out_bf16<HPW, true, true><<<ogrid, 256, 0, stream>>>(q, ldq, gq, Sop, zop, r_q, N, H, eps,
+                                                                             inv_C, out, ldo));
+    } else {
+      SANA_LAUNCH("out", out_bf16<HPW, false, true><<<ogrid, 256, 0, stream>>>(q, ldq, nullptr, Sop, zop, nullptr, N, H,
+                                                                              eps, inv_C, out, ldo));
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sanala

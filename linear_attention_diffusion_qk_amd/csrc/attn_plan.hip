@@ -1,0 +1,79 @@
+// Launch planning and dtype dispatch of the linear attention.
+#include "attn.h"
+
+#include <algorithm>
+#include <cstdlib>
+
+namespace sanala {
+
+namespace {
+constexpr size_t kPartStrideBytes = (kHeadDim * kHeadDim + kHeadDim) * 4;
+constexpr size_t kMaxLds = 160 * 1024;  // LDS per CU on gfx950
+
+int env_int(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  const int v = std::atoi(s);
+  return v > 0 ? v : dflt;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int device_cus() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      v > 0)
+    return v;
+  return 256;
+}
+}  // namespace
+
+int max_heads() { return 320; }  // the fp32 output kernel stages 4 rows of C floats in LDS
+
+AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
+  AttnPlan p{};
+  p.B = B;
+  p.N = N;
+  p.H = H;
+  p.dtype = dtype;
+  p.norm = norm;
+  p.num_cus = device_cus();
+  const bool bf = dtype == kDtypeBf16;
+  // KV chunking: about 1024 blocks in total, chunks of at least 256 tokens (the partial state costs
+  // 33/Tc of the K+V traffic), never more than the sequence.
+  const int groups = bf ? (H + 1) / 2 : H;
+  const int64_t per_chunk = (int64_t)B * groups;
+  const int nc = (int)std::max<int64_t>(1, (1024 + per_chunk - 1) / per_chunk);
+  const int n64 = (N + 63) / 64 * 64;
+  int Tc = ((N + nc - 1) / nc + 63) / 64 * 64;
+  Tc = std::max(Tc, std::min(256, n64));
+  Tc = env_int("SANA_KV_CHUNK", Tc);
+  Tc = std::max(64, (Tc + 63) / 64 * 64);
+  p.Tc = Tc;
+  p.NC = (N + Tc - 1) / Tc;
+  p.out_persistent = bf && H <= 80 && out_persist_lds_bytes(H) <= kMaxLds &&
+                     (int64_t)B * ((N + 15) / 16) >= 2 * p.num_cus && env_int("SANA_OUT_PERSIST", 1) == 1;
+  const size_t BH = (size_t)B * H;
+  size_t off = 0;
+  p.off_rk = off;   off = align_up(off + (norm ? (size_t)B * N * 4 : 0), 256);
+  p.off_rq = off;   off = align_up(off + (norm && bf && H > 72 ? (size_t)B * N * 4 : 0), 256);
+  p.off_part = off; off = align_up(off + (p.NC > 1 || !bf ? BH * p.NC * kPartStrideBytes : 0), 256);
+  p.off_S32 = off;  off = align_up(off + (bf ? 0 : BH * kHeadDim * kHeadDim * 4), 256);
+  p.off_z = off;    off = align_up(off + (bf ? 0 : BH * kHeadDim * 4), 256);
+  p.off_Sop = off;  off = align_up(off + (bf ? bf16_operand_bytes((int64_t)BH) : 0), 256);
+  p.ws_bytes = off;
+  return p;
+}
+
+hipError_t launch_attn(const AttnPlan& p, const void* q, int64_t ldq, const void* k, const void* v, int64_t ldkv,
+                       const float* gq, const float* gk, float eps, void* out, int64_t ldo, void* ws,
+                       hipStream_t stream) {
+  if (p.dtype == kDtypeF32)
+    return launch_attn_f32(p, static_cast<const float*>(q), ldq, static_cast<const float*>(k),
+                           static_cast<const float*>(v), ldkv, gq, gk, eps, static_cast<float*>(out), ldo, ws, stream);
+  return launch_attn_bf16(p, static_cast<const uint16_t*>(q), ldq, static_cast<const uint16_t*>(k),
+                          static_cast<const uint16_t*>(v), ldkv, gq, gk, eps, static_cast<uint16_t*>(out), ldo, ws,
+                          p.num_cus, stream);
+}
+
+}  // namespace sanala

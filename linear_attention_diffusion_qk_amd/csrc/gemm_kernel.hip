@@ -122,7 +122,7 @@ hipError_t launch_qkv_gemm(const uint16_t* x, const uint16_t* w, uint16_t* qkv, 
   const int NO = 3 * C;
   if (C % 8 != 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((M + BM - 1) / BM), (NO + BN - 1) / BN);
-  qkv_gemm_kernel<<<grid, kThreads, 0, stream>>>(x, w, qkv, M, C, NO);
+  SANA_LAUNCH("qkv_gemm", qkv_gemm_kernel<<<grid, kThreads, 0, stream>>>(x, w, qkv, M, C, NO));
   return hipGetLastError();
 }
 

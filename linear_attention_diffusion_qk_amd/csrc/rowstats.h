@@ -1,0 +1,36 @@
+// Row statistics kernel shared by the fp32 and bf16 paths.
+#pragma once
+
+#include "common.h"
+
+namespace sanala {
+
+// r[row] = 1 / sqrt(mean_c x[row, c]^2 + eps) over all C channels of a token row (the QK-Norm
+// scale), one wave per row, 16-byte loads.  Rows are `ld` elements apart.
+template <typename T>
+__global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ x, int64_t ld, int64_t rows, int C,
+                                                       float eps, float* __restrict__ r) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const char* p = reinterpret_cast<const char*>(x + row * ld);
+  const int nvec = C * (int)sizeof(T) / 16;
+  float ss = 0.f;
+  for (int i = lane; i < nvec; i += 64) {
+    const u32x4 w = load16(p + 16 * (int64_t)i);
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ss = dot2_bf16(w[u], w[u], ss);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float a = __uint_as_float(w[u]);
+        ss = fmaf(a, a, ss);
+      }
+    }
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) r[row] = 1.0f / sqrtf(ss / (float)C + eps);
+}
+
+}  // namespace sanala

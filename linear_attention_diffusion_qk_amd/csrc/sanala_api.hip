@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <mutex>
+#include <vector>
 
 namespace {
 
@@ -38,7 +39,7 @@ sana_status_t check_common(int B, int N, int H, int D, float eps, const float* g
   if (!std::isfinite(eps) || eps < 0.f) return SANA_ERR_INVALID_ARG;
   if ((gq == nullptr) != (gk == nullptr)) return SANA_ERR_INVALID_ARG;
   if (D != sanala::kHeadDim) return SANA_ERR_UNSUPPORTED;
-  if (H > sanala::out_bf16_max_heads()) return SANA_ERR_UNSUPPORTED;
+  if (H > sanala::max_heads()) return SANA_ERR_UNSUPPORTED;
   if (B > 65535) return SANA_ERR_UNSUPPORTED;
   const double elems = (double)B * (double)N * (double)H * (double)D;
   if (elems >= 1099511627776.0) return SANA_ERR_UNSUPPORTED;  // 2^40
@@ -46,7 +47,64 @@ sana_status_t check_common(int B, int N, int H, int D, float eps, const float* g
   return SANA_OK;
 }
 
+// Per-host-thread kernel timing (measurement support).
+struct TimedKernel {
+  const char* name;
+  hipEvent_t begin, end;
+};
+struct Timing {
+  bool enabled = false;
+  int count = 0;
+  std::vector<TimedKernel> slots;
+  ~Timing() {
+    for (auto& t : slots) {
+      (void)hipEventDestroy(t.begin);
+      (void)hipEventDestroy(t.end);
+    }
+  }
+};
+thread_local Timing g_timing;
+
 }  // namespace
+
+namespace sanala {
+void timing_begin(const char* name, hipStream_t s) {
+  Timing& T = g_timing;
+  if (!T.enabled) return;
+  if (T.count == (int)T.slots.size()) {
+    TimedKernel k{name, nullptr, nullptr};
+    if (hipEventCreate(&k.begin) != hipSuccess || hipEventCreate(&k.end) != hipSuccess) return;
+    T.slots.push_back(k);
+  }
+  T.slots[T.count].name = name;
+  (void)hipEventRecord(T.slots[T.count].begin, s);
+}
+void timing_end(hipStream_t s) {
+  Timing& T = g_timing;
+  if (!T.enabled || T.count >= (int)T.slots.size()) return;
+  (void)hipEventRecord(T.slots[T.count].end, s);
+  ++T.count;
+}
+}  // namespace sanala
+
+extern "C" sana_status_t sana_timing_enable(int enable) {
+  g_timing.enabled = enable != 0;
+  g_timing.count = 0;
+  return SANA_OK;
+}
+
+extern "C" int sana_timing_last(const char** names, float* ms, int capacity) {
+  Timing& T = g_timing;
+  int n = 0;
+  for (; n < T.count && n < capacity; ++n) {
+    float t = -1.f;
+    if (hipEventSynchronize(T.slots[n].end) == hipSuccess)
+      (void)hipEventElapsedTime(&t, T.slots[n].begin, T.slots[n].end);
+    if (names) names[n] = T.slots[n].name;
+    if (ms) ms[n] = t;
+  }
+  return T.count;
+}
 
 extern "C" const char* sana_status_string(sana_status_t s) {
   switch (s) {
@@ -75,6 +133,7 @@ extern "C" sana_status_t sana_linear_attn_fwd(const void* q, const void* k, cons
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return SANA_ERR_HIP;
   init_pool(dev);
+  g_timing.count = 0;
   const bool norm = gq != nullptr;
   const int dt = dtype == SANA_BF16 ? sanala::kDtypeBf16 : sanala::kDtypeF32;
   const sanala::AttnPlan plan = sanala::plan_attn(B, N, H, dt, norm);
@@ -102,6 +161,7 @@ extern "C" sana_status_t sana_qkv_linear_attn_fwd(const void* x, const void* Wqk
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return SANA_ERR_HIP;
   init_pool(dev);
+  g_timing.count = 0;
   const bool norm = gq != nullptr;
   const sanala::AttnPlan plan = sanala::plan_attn(B, N, H, sanala::kDtypeBf16, norm);
   const size_t qkv_bytes = ((size_t)M * 3 * C * 2 + 255) / 256 * 256;

@@ -36,13 +36,14 @@ def _rng(cfg_id: int, sample: int, tid: int) -> np.random.Generator:
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """uint16 bit patterns of x rounded to bf16, round-to-nearest-even; NaN stays NaN (quieted)."""
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    lsb = (b >> np.uint64(16)) & np.uint64(1)
-    r = ((b + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) & np.uint64(0xFFFF)
-    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    b = x32.view(np.uint32)
+    # for every non-NaN pattern b + 0x8000 stays below 2^32, so uint32 arithmetic cannot wrap
+    r = ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x32)
     if nan.any():
-        r[nan] = ((b[nan] >> np.uint64(16)) | np.uint64(0x40)) & np.uint64(0xFFFF)
-    return r.astype(np.uint16)
+        r[nan] = ((b[nan] >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16)
+    return r
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
