@@ -11,6 +11,8 @@ reduction and output: the whole path).
 
   python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload config4|config2|config3|config5]
   python bench.py --mode copy        # plain device copy of known size (counter calibration under rocprofv3)
+  python bench.py --summarize-traffic KERNEL_FETCH.db KERNEL_WRITE.db COPY_FETCH.db COPY_WRITE.db
+                                     # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE databases -> profiles/hbm_traffic.txt
 """
 from __future__ import annotations
 
@@ -105,7 +107,7 @@ class Inputs:
 
     def kernel_bytes(self, kernel: str) -> float:
         tok = self.B * self.N * self.C * 2
-        if kernel == "kv_partial":
+        if kernel in ("kv_state", "kv_partial"):
             return 2 * tok            # read K and V
         if kernel == "out":
             return 2 * tok            # read Q, write O
@@ -181,7 +183,60 @@ def run_copy_calibration():
     print(json.dumps({"mode": "copy", "bytes_per_launch": n}))
 
 
+def _pmc_means(db: str, counter: str):
+    """Mean counter value per kernel name in a rocprofv3 --pmc database."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute("select kernel_name, value from counters_collection where counter_name = ?", (counter,)).fetchall()
+    acc = {}
+    for name, val in rows:
+        acc.setdefault(name, []).append(float(val))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def summarize_traffic(kfetch: str, kwrite: str, cfetch: str, cwrite: str, workload: str = "config4") -> str:
+    """Per-dispatch HBM bytes of each libsanala kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    scaled by what the same counters read for a plain device copy of 268,435,456 bytes."""
+    copy_bytes = 256 * 1024 * 1024
+    pick = lambda d: max((v for k, v in d.items() if "copy" in k.lower() or "elementwise" in k.lower()), default=None)  # noqa: E731
+    cf, cw = pick(_pmc_means(cfetch, "FETCH_SIZE")), pick(_pmc_means(cwrite, "WRITE_SIZE"))
+    f_scale = copy_bytes / (cf * 1024.0)
+    w_scale = copy_bytes / (cw * 1024.0)
+    kf, kw = _pmc_means(kfetch, "FETCH_SIZE"), _pmc_means(kwrite, "WRITE_SIZE")
+    lines = ["# HBM traffic per dispatch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (separate runs).",
+             "# Counter KiB x 1024 x calibration; calibration = 268435456 / (counter bytes of a plain",
+             "# device copy of 268435456 bytes, bench.py --mode copy).",
+             "# Commands (from /tmp, TMPDIR=/tmp, one pass each):",
+             "#   rocprofv3 --pmc FETCH_SIZE -d kfetch -o run -- python3 /root/repo/bench.py --steps 3 --warmup 1 "
+             "--no-cpu-baseline --no-secondary",
+             "#   rocprofv3 --pmc WRITE_SIZE -d kwrite -o run -- (same bench command)",
+             "#   rocprofv3 --pmc FETCH_SIZE -d cfetch -o run -- python3 /root/repo/bench.py --mode copy",
+             "#   rocprofv3 --pmc WRITE_SIZE -d cwrite -o run -- python3 /root/repo/bench.py --mode copy",
+             "#   python3 bench.py --summarize-traffic kfetch/run_results.db kwrite/run_results.db "
+             "cfetch/run_results.db cwrite/run_results.db",
+             f"workload: {workload}", f"source_hash: {source_hash()}",
+             f"fetch_calibration: {f_scale:.4f}", f"write_calibration: {w_scale:.4f}"]
+    short = {"rowstats": "rowstats_k", "kv_state": "kv_state", "kv_reduce": "kv_reduce", "out_persist": "out",
+             "out_bf16": "out", "qkv_gemm": "qkv_gemm"}
+    for name in sorted(set(kf) | set(kw)):
+        tag = next((v for k, v in short.items() if k in name), None)
+        if tag is None or "sanala" not in name:
+            continue
+        fb = kf.get(name, 0.0) * 1024.0 * f_scale
+        wb = kw.get(name, 0.0) * 1024.0 * w_scale
+        lines.append(f"{tag}_fetch_bytes_per_launch: {fb:.0f}")
+        lines.append(f"{tag}_write_bytes_per_launch: {wb:.0f}")
+        lines.append(f"{tag}_bytes_per_launch: {fb + wb:.0f}")
+    return "\n".join(lines) + "\n"
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-traffic":
+        text = summarize_traffic(*sys.argv[2:6])
+        with open(os.path.join(ROOT, "profiles", "hbm_traffic.txt"), "w") as f:
+            f.write(text)
+        print(text)
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)

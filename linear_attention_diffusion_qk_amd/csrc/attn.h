@@ -38,7 +38,7 @@ hipError_t launch_attn_bf16(const AttnPlan& p, const uint16_t* q, int64_t ldq, c
                             int64_t ldkv, const float* gq, const float* gk, float eps, uint16_t* out, int64_t ldo,
                             void* ws, int num_cus, hipStream_t stream);
 size_t out_persist_lds_bytes(int H);
-size_t bf16_operand_bytes(int64_t BH);
+size_t bf16_operand_bytes(int64_t BH, int H);
 
 int max_heads();
 

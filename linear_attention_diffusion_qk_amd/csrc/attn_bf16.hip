@@ -44,6 +44,14 @@ __device__ __forceinline__ int sop_index(int d, int e) {
   return eb * 512 + (m + 16 * kg) * 8 + j;
 }
 
+// Sign masks (0x8000 per negative gain) of query dims 8kg + 2u, 8kg + 2u + 1 of head h.
+template <bool NORM>
+__device__ __forceinline__ uint32_t sign_word(const float* __restrict__ gq, int h, int kg, int u) {
+  if (!NORM) return 0u;
+  const int d0 = h * kHeadDim + 8 * kg + 2 * u;
+  return (gq[d0] < 0.f ? 0x8000u : 0u) | (gq[d0 + 1] < 0.f ? 0x80000000u : 0u);
+}
+
 // Writes one reduced state element (i < 1024: S~[i/32][i%32]; else z~[i-1024]) of head h of sample
 // row bh as the output kernel's operands, scaled by G_d = |gq_d| |gk_d| (1 without the norm).
 template <bool NORM>
@@ -74,7 +82,8 @@ __global__ __launch_bounds__(256) void kv_state_bf16(const uint16_t* __restrict_
                                                      int64_t ld, const float* __restrict__ r_k,
                                                      const float* __restrict__ gq, const float* __restrict__ gk,
                                                      int N, int H, int Tc, int NC, float* __restrict__ part,
-                                                     uint16_t* __restrict__ Sop, uint16_t* __restrict__ zop) {
+                                                     uint16_t* __restrict__ Sop, uint16_t* __restrict__ zop,
+                                                     uint32_t* __restrict__ gsg) {
   constexpr int SB = 64;     // tokens per sub-block
   constexpr int PITCH = 72;  // bf16 per staged row (64 used)
   __shared__ __attribute__((aligned(16))) uint16_t Ks[SB * PITCH];
@@ -187,6 +196,10 @@ __global__ __launch_bounds__(256) void kv_state_bf16(const uint16_t* __restrict_
       const int hl = i / kPartStride, off = i - hl * kPartStride;
       emit_state<NORM>(bh0 + hl, h0 + hl, off, fin[i], gq, gk, Sop, zop);
     }
+    if (b == 0 && tid < nh * kSgnPerHead) {
+      const int h = h0 + tid / kSgnPerHead, i = tid % kSgnPerHead;
+      gsg[h * kSgnPerHead + i] = sign_word<NORM>(gq, h, i / 4, i & 3);
+    }
     return;
   }
   for (int i = tid; i < nh * kPartStride; i += 256) {
@@ -200,22 +213,25 @@ __global__ __launch_bounds__(256) void kv_state_bf16(const uint16_t* __restrict_
 template <bool NORM>
 __global__ __launch_bounds__(256) void kv_reduce_bf16(const float* __restrict__ part, int NC, int H, int64_t BH,
                                                       const float* __restrict__ gq, const float* __restrict__ gk,
-                                                      uint16_t* __restrict__ Sop, uint16_t* __restrict__ zop) {
+                                                      uint16_t* __restrict__ Sop, uint16_t* __restrict__ zop,
+                                                      uint32_t* __restrict__ gsg) {
   const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gi < (int64_t)H * kSgnPerHead)
+    gsg[gi] = sign_word<NORM>(gq, (int)(gi / kSgnPerHead), (int)(gi / 4) & 3, (int)gi & 3);
   if (gi >= BH * kPartStride) return;
   const int64_t bh = gi / kPartStride;
   const int i = (int)(gi - bh * kPartStride);
   const float* src = part + bh * NC * kPartStride + i;
+  // All loads of a batch are issued before the in-order sum.
   float s = 0.f;
-  int c = 0;
-  for (; c + 8 <= NC; c += 8) {
-    float x[8];
+  for (int c = 0; c < NC; c += 32) {
+    float x[32];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = src[(int64_t)(c + u) * kPartStride];
+    for (int u = 0; u < 32; ++u) x[u] = c + u < NC ? src[(int64_t)(c + u) * kPartStride] : 0.f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s += x[u];
+    for (int u = 0; u < 32; ++u)
+      if (c + u < NC) s += x[u];
   }
-  for (; c < NC; ++c) s += src[(int64_t)c * kPartStride];
   emit_state<NORM>(bh, (int)(bh % H), i, s, gq, gk, Sop, zop);
 }
 
@@ -244,12 +260,17 @@ __device__ __forceinline__ u32x4 head_out(u32x4 qv, u32x4 sg, bf16x8 a0, bf16x8 
                cvt_pk_bf16(o1[0] * inv, o1[1] * inv), cvt_pk_bf16(o1[2] * inv, o1[3] * inv)};
 }
 
-// Sign masks (0x8000 per negative gain) of query dims 8kg + 2u, 8kg + 2u + 1 of head h.
-template <bool NORM>
-__device__ __forceinline__ uint32_t sign_word(const float* __restrict__ gq, int h, int kg, int u) {
-  if (!NORM) return 0u;
-  const int d0 = h * kHeadDim + 8 * kg + 2 * u;
-  return (gq[d0] < 0.f ? 0x8000u : 0u) | (gq[d0 + 1] < 0.f ? 0x80000000u : 0u);
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Copies `bytes` (a multiple of 16) from global memory to LDS with direct global->LDS loads; waves
+// take 1 KB chunks round robin.  The caller waits (s_waitcnt) and synchronises before reading.
+__device__ __forceinline__ void dma_to_lds(const void* src, void* lds, int bytes, int w, int nw, int lane) {
+  const char* s = static_cast<const char*>(src);
+  char* d = static_cast<char*>(lds);
+  for (int c = w; c * 1024 < bytes; c += nw) {
+    const int off = c * 1024 + lane * 16;
+    if (off < bytes) __builtin_amdgcn_global_load_lds(s + off, (lds_ptr_t)(d + c * 1024), 16, 0, 0);
+  }
 }
 
 // Lane swap between the two 8-lane halves of every 16-lane row (DPP row_ror:8): lanes whose bank
@@ -279,7 +300,8 @@ __device__ __forceinline__ u32x4 swap_halves(u32x4 old, u32x4 src) {
 // ---------------------------------------------------------------------------------------------
 template <int PPW, bool NORM>
 __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restrict__ q, int64_t ldq,
-                                                        const float* __restrict__ gq, const uint16_t* __restrict__ Sop,
+                                                        const uint32_t* __restrict__ gsg,
+                                                        const uint16_t* __restrict__ Sop,
                                                         const uint16_t* __restrict__ zop, int B, int N, int H, float eps,
                                                         float inv_C, uint16_t* __restrict__ out, int64_t ldo,
                                                         int tiles_per_block) {
@@ -298,9 +320,6 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
   const int64_t tau0 = (int64_t)blockIdx.x * tiles_per_block;
   const int64_t tau_end = min(total, tau0 + tiles_per_block);
   if (tau0 >= tau_end) return;
-
-  for (int i = tid; i < H * kSgnPerHead; i += NW * 64)
-    Gs[i] = sign_word<NORM>(gq, i / kSgnPerHead, (i / 4) & 3, i & 3);
 
   // Raw loads of one tile: qr[2*i + j] = load j of pair w*PPW + i.  Addresses are clamped into the
   // tensor; lanes past N or H are never stored.
@@ -323,20 +342,12 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
     const int n0 = (int)(tau - bb * tiles_per_sample) * 16;
     if (bb != cur_b) {  // uniform across the block
       __syncthreads();
-      const u32x4* s1 = reinterpret_cast<const u32x4*>(Sop + bb * H * kOpPerHead);
-      u32x4* d1 = reinterpret_cast<u32x4*>(Ss);
-      const int n1 = H * kOpPerHead / 8;
-      for (int i0 = tid; i0 < n1; i0 += 8 * NW * 64) {
-        u32x4 tmp[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) tmp[u] = s1[min(i0 + u * NW * 64, n1 - 1)];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (i0 + u * NW * 64 < n1) d1[i0 + u * NW * 64] = tmp[u];
-      }
-      const u32x4* s2 = reinterpret_cast<const u32x4*>(zop + bb * H * kZopPerHead);
-      u32x4* d2 = reinterpret_cast<u32x4*>(Zs);
-      for (int i = tid; i < H * kZopPerHead / 8; i += NW * 64) d2[i] = s2[i];
+      // S' and z' of the sample go straight from global memory to LDS (global_load_lds_dwordx4:
+      // 1 KB per wave instruction, lane l writing bytes [16l, 16l + 16) of the chunk).
+      dma_to_lds(Sop + bb * H * kOpPerHead, Ss, H * kOpPerHead * 2, w, NW, lane);
+      dma_to_lds(zop + bb * H * kZopPerHead, Zs, H * kZopPerHead * 2, w, NW, lane);
+      if (cur_b < 0) dma_to_lds(gsg, Gs, H * kSgnPerHead * 4, w, NW, lane);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       cur_b = bb;
     }
@@ -407,7 +418,7 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
 // ---------------------------------------------------------------------------------------------
 template <int HPW, bool NORM, bool PRE_R>
 __global__ __launch_bounds__(256) void out_bf16(const uint16_t* __restrict__ q, int64_t ldq,
-                                                const float* __restrict__ gq, const uint16_t* __restrict__ Sop,
+                                                const uint32_t* __restrict__ gsg, const uint16_t* __restrict__ Sop,
                                                 const uint16_t* __restrict__ zop, const float* __restrict__ r_q, int N,
                                                 int H, float eps, float inv_C, uint16_t* __restrict__ out,
                                                 int64_t ldo) {
@@ -446,8 +457,7 @@ __global__ __launch_bounds__(256) void out_bf16(const uint16_t* __restrict__ q, 
     if (i < hcnt) {
       const int h = hbeg + i;
       const int64_t bh = (int64_t)b * H + h;
-      const u32x4 sg = {sign_word<NORM>(gq, h, kg, 0), sign_word<NORM>(gq, h, kg, 1), sign_word<NORM>(gq, h, kg, 2),
-                        sign_word<NORM>(gq, h, kg, 3)};
+      const u32x4 sg = load16(gsg + h * kSgnPerHead + kg * 4);
       const uint16_t* sh = Sop + bh * kOpPerHead + lane * 8;
       const uint16_t* zh = zop + bh * kZopPerHead + kg * 8;
       const u32x4 o = head_out(qr[i], sg, as_bf16x8(load16(sh)), as_bf16x8(load16(sh + 512)), load16(zh),
@@ -465,7 +475,9 @@ size_t out_persist_lds_bytes(int H) {
   return (size_t)H * (kOpPerHead * 2 + kZopPerHead * 2 + kSgnPerHead * 4) + 2 * 8 * 16 * 4;
 }
 
-size_t bf16_operand_bytes(int64_t BH) { return (size_t)BH * (kOpPerHead + kZopPerHead) * 2; }
+size_t bf16_operand_bytes(int64_t BH, int H) {
+  return (size_t)BH * (kOpPerHead + kZopPerHead) * 2 + (size_t)H * kSgnPerHead * 4;
+}
 
 constexpr int kPersistPPW = 5;  // head pairs per wave in the persistent output kernel (<= 8 waves: H <= 80)
 
@@ -477,6 +489,7 @@ hipError_t launch_attn_bf16(const AttnPlan& p, const uint16_t* q, int64_t ldq, c
   float* part = reinterpret_cast<float*>(base + p.off_part);
   uint16_t* Sop = reinterpret_cast<uint16_t*>(base + p.off_Sop);
   uint16_t* zop = Sop + (size_t)p.B * p.H * kOpPerHead;
+  uint32_t* gsg = reinterpret_cast<uint32_t*>(zop + (size_t)p.B * p.H * kZopPerHead);
   const int B = p.B, N = p.N, H = p.H, C = H * kHeadDim;
   const int64_t rows = (int64_t)B * N;
   const int64_t BH = (int64_t)B * H;
@@ -487,17 +500,18 @@ hipError_t launch_attn_bf16(const AttnPlan& p, const uint16_t* q, int64_t ldq, c
   const dim3 grid(p.NC, (H + 1) / 2, B);
   if (p.norm)
     SANA_LAUNCH("kv_state", kv_state_bf16<true><<<grid, 256, 0, stream>>>(k, v, ldkv, r_k, gq, gk, N, H, p.Tc, p.NC,
-                                                                          part, Sop, zop));
+                                                                          part, Sop, zop, gsg));
   else
     SANA_LAUNCH("kv_state", kv_state_bf16<false><<<grid, 256, 0, stream>>>(k, v, ldkv, nullptr, nullptr, nullptr, N, H,
-                                                                           p.Tc, p.NC, part, Sop, zop));
+                                                                           p.Tc, p.NC, part, Sop, zop, gsg));
   if (p.NC > 1) {
     const unsigned blocks = (unsigned)((BH * kPartStride + 255) / 256);
     if (p.norm)
-      SANA_LAUNCH("kv_reduce", kv_reduce_bf16<true><<<blocks, 256, 0, stream>>>(part, p.NC, H, BH, gq, gk, Sop, zop));
+      SANA_LAUNCH("kv_reduce",
+                  kv_reduce_bf16<true><<<blocks, 256, 0, stream>>>(part, p.NC, H, BH, gq, gk, Sop, zop, gsg));
     else
       SANA_LAUNCH("kv_reduce",
-                  kv_reduce_bf16<false><<<blocks, 256, 0, stream>>>(part, p.NC, H, BH, nullptr, nullptr, Sop, zop));
+                  kv_reduce_bf16<false><<<blocks, 256, 0, stream>>>(part, p.NC, H, BH, nullptr, nullptr, Sop, zop, gsg));
   }
 
   const float inv_C = 1.0f / (float)C;
@@ -518,30 +532,30 @@ hipError_t launch_attn_bf16(const AttnPlan& p, const uint16_t* q, int64_t ldq, c
     }
     if (p.norm)
       SANA_LAUNCH("out", out_persist_bf16<kPersistPPW, true><<<nblk, nw * 64, lds, stream>>>(
-                             q, ldq, gq, Sop, zop, B, N, H, eps, inv_C, out, ldo, per));
+                             q, ldq, gsg, Sop, zop, B, N, H, eps, inv_C, out, ldo, per));
     else
       SANA_LAUNCH("out", out_persist_bf16<kPersistPPW, false><<<nblk, nw * 64, lds, stream>>>(
-                             q, ldq, nullptr, Sop, zop, B, N, H, eps, inv_C, out, ldo, per));
+                             q, ldq, gsg, Sop, zop, B, N, H, eps, inv_C, out, ldo, per));
     return hipGetLastError();
   }
   constexpr int HPW = 18;
   if (H <= 4 * HPW) {
     const dim3 ogrid((N + 15) / 16, B, 1);
     if (p.norm)
-      SANA_LAUNCH("out", out_bf16<HPW, true, false><<<ogrid, 256, 0, stream>>>(q, ldq, gq, Sop, zop, nullptr, N, H, eps,
+      SANA_LAUNCH("out", out_bf16<HPW, true, false><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, nullptr, N, H, eps,
                                                                               inv_C, out, ldo));
     else
-      SANA_LAUNCH("out", out_bf16<HPW, false, false><<<ogrid, 256, 0, stream>>>(q, ldq, nullptr, Sop, zop, nullptr, N, H,
+      SANA_LAUNCH("out", out_bf16<HPW, false, false><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, nullptr, N, H,
                                                                                eps, inv_C, out, ldo));
   } else {
     const dim3 ogrid((N + 15) / 16, B, (H + 4 * HPW - 1) / (4 * HPW));
     float* r_q = reinterpret_cast<float*>(base + p.off_rq);
     if (p.norm) {
       SANA_LAUNCH("rowstats_q", rowstats_kernel<uint16_t><<<rs_blocks, 256, 0, stream>>>(q, ldq, rows, C, eps, r_q));
-      SANA_LAUNCH("out", out_bf16<HPW, true, true><<<ogrid, 256, 0, stream>>>(q, ldq, gq, Sop, zop, r_q, N, H, eps,
+      SANA_LAUNCH("out", out_bf16<HPW, true, true><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, r_q, N, H, eps,
                                                                              inv_C, out, ldo));
     } else {
-      SANA_LAUNCH("out", out_bf16<HPW, false, true><<<ogrid, 256, 0, stream>>>(q, ldq, nullptr, Sop, zop, nullptr, N, H,
+      SANA_LAUNCH("out", out_bf16<HPW, false, true><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, nullptr, N, H,
                                                                               eps, inv_C, out, ldo));
     }
   }

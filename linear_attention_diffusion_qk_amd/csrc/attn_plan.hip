@@ -60,7 +60,7 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
   p.off_part = off; off = align_up(off + (p.NC > 1 || !bf ? BH * p.NC * kPartStrideBytes : 0), 256);
   p.off_S32 = off;  off = align_up(off + (bf ? 0 : BH * kHeadDim * kHeadDim * 4), 256);
   p.off_z = off;    off = align_up(off + (bf ? 0 : BH * kHeadDim * 4), 256);
-  p.off_Sop = off;  off = align_up(off + (bf ? bf16_operand_bytes((int64_t)BH) : 0), 256);
+  p.off_Sop = off;  off = align_up(off + (bf ? bf16_operand_bytes((int64_t)BH, H) : 0), 256);
   p.ws_bytes = off;
   return p;
 }
