@@ -11,6 +11,8 @@ namespace sanala {
 constexpr int kHeadDim = 32;  // D: the only head size with kernels
 constexpr int kDtypeF32 = 0;
 constexpr int kDtypeBf16 = 1;
+constexpr int kOutPersist = 1;  // bf16 output: one block per CU, all heads, operands in LDS
+constexpr int kOutTile = 2;     // bf16 output: 16-token tiles over all heads, operands from global memory
 
 // Launch plan and scratch layout of one attention call.
 struct AttnPlan {
@@ -18,7 +20,7 @@ struct AttnPlan {
   bool norm;
   int Tc;               // tokens per KV chunk (multiple of 64)
   int NC;               // number of chunks per sample
-  bool out_persistent;  // bf16 output through the persistent LDS-resident-state kernel
+  int out_kind;         // bf16 output kernel: kOutPersist or kOutTile
   int num_cus;          // compute units of the current device
   size_t off_rk, off_rq, off_part, off_S32, off_z, off_Sop;
   size_t ws_bytes;

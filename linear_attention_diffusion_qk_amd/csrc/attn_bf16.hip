@@ -242,7 +242,7 @@ __global__ __launch_bounds__(256) void kv_reduce_bf16(const float* __restrict__ 
 // Returns output channels 8kg..8kg+7 of token t as bf16 (1/den by v_rcp_f32, 1 ulp).
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ u32x4 head_out(u32x4 qv, u32x4 sg, bf16x8 a0, bf16x8 a1, u32x4 zh, u32x4 zl, float epsr,
-                                          bool even_row) {
+                                          bool even_row, float* den = nullptr) {
   u32x4 psi;
 #pragma unroll
   for (int u = 0; u < 4; ++u) psi[u] = relu_bf16x2(qv[u] ^ sg[u]);
@@ -255,7 +255,9 @@ __device__ __forceinline__ u32x4 head_out(u32x4 qv, u32x4 sg, bf16x8 a0, bf16x8 
   o0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, Bq, o0, 0, 0, 0);
   o1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, Bq, o1, 0, 0, 0);
   oz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(zsel), Bq, oz, 0, 0, 0);
-  const float inv = __builtin_amdgcn_rcpf((oz[0] + oz[1]) + epsr);
+  const float d = oz[0] + oz[1];
+  if (den) *den = d;
+  const float inv = __builtin_amdgcn_rcpf(d + epsr);
   return u32x4{cvt_pk_bf16(o0[0] * inv, o0[1] * inv), cvt_pk_bf16(o0[2] * inv, o0[3] * inv),
                cvt_pk_bf16(o1[0] * inv, o1[1] * inv), cvt_pk_bf16(o1[2] * inv, o1[3] * inv)};
 }
@@ -376,10 +378,16 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
       for (int ww = 0; ww < NW; ++ww) tot += sb[ww * 16 + n16];
       epsr = eps * sqrtf(tot * inv_C + eps);  // eps / r_q
     }
+    // Output rows of this tile as one range-checked buffer: every store instruction is issued (lanes
+    // past N or H get an out-of-range offset), so the store count per step is fixed and the waits for
+    // the next tile's loads never include this tile's stores.
+    const int rows = min(16, N - n0);
+    const __amdgpu_buffer_rsrc_t orsrc =
+        make_rsrc(out + (bb * N + n0) * ldo, (uint32_t)(((rows - 1) * ldo + (int64_t)H * kHeadDim) * 2));
 #pragma unroll
     for (int i = 0; i < PPW; ++i) {
       const int h0 = 2 * (w * PPW + i);
-      if (h0 < H) {
+      {
         u32x4 o[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -395,19 +403,44 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
         const int h = h0 + hsel;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int n = n0 + 8 * j + tok8;
-          if (n < N && h < H) store16(out + (bb * N + n) * ldo + h * kHeadDim + kg * 8, st[j]);
+          const int r = 8 * j + tok8;
+          const uint32_t off = (r < rows && h < H) ? (uint32_t)((r * ldo + h * kHeadDim + kg * 8) * 2) : kOutOfRange;
+          buffer_store16(orsrc, off, st[j]);
         }
       }
     }
   };
 
   u32x4 qa[2 * PPW], qb[2 * PPW];
-  load_tile(tau0, qa);
-  for (int64_t tau = tau0; tau < tau_end; tau += 2) {
-    step(tau, qa, qb);
-    if (tau + 1 < tau_end) step(tau + 1, qb, qa);
+  {
+    // The first sample's operands are requested ahead of the first Q tile so that the wait below
+    // covers only them (vmcnt retires in issue order): the tile's loads stay in flight.
+    const int64_t b0 = tau0 / tiles_per_sample;
+    dma_to_lds(Sop + b0 * H * kOpPerHead, Ss, H * kOpPerHead * 2, w, NW, lane);
+    dma_to_lds(zop + b0 * H * kZopPerHead, Zs, H * kZopPerHead * 2, w, NW, lane);
+    dma_to_lds(gsg, Gs, H * kSgnPerHead * 4, w, NW, lane);
+    __asm__ __volatile__("" ::: "memory");
+    load_tile(tau0, qa);
+    __asm__ __volatile__("" ::: "memory");
+    static_assert(2 * PPW <= 15, "vmcnt immediate holds 4 low bits here");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * PPW));  // vmcnt <= 2*PPW, expcnt/lgkmcnt not waited on
+    // A bare s_barrier: __syncthreads() would also wait for the tile's loads.
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+    cur_b = b0;
   }
+  // The first step is peeled so that the loop is entered, like its back edge, with one tile's loads and
+  // one tile's stores outstanding; both loop steps run unconditionally.  With no control-flow merge of
+  // different outstanding counts the compiler's waits for a tile's loads never cover earlier stores.
+  int64_t tau = tau0;
+  step(tau, qa, qb);
+  ++tau;
+  for (; tau + 1 < tau_end; tau += 2) {
+    step(tau, qb, qa);
+    step(tau + 1, qa, qb);
+  }
+  if (tau < tau_end) step(tau, qb, qa);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -515,7 +548,7 @@ hipError_t launch_attn_bf16(const AttnPlan& p, const uint16_t* q, int64_t ldq, c
   }
 
   const float inv_C = 1.0f / (float)C;
-  if (p.out_persistent) {
+  if (p.out_kind == kOutPersist) {
     const int64_t tiles = (int64_t)B * ((N + 15) / 16);
     const int blocks = (int)std::min<int64_t>(num_cus, tiles);
     const int per = (int)((tiles + blocks - 1) / blocks);

@@ -51,8 +51,12 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
   Tc = std::max(64, (Tc + 63) / 64 * 64);
   p.Tc = Tc;
   p.NC = (N + Tc - 1) / Tc;
-  p.out_persistent = bf && H <= 80 && out_persist_lds_bytes(H) <= kMaxLds &&
-                     (int64_t)B * ((N + 15) / 16) >= 2 * p.num_cus && env_int("SANA_OUT_PERSIST", 1) == 1;
+  // bf16 output kernel: persistent when the sample's operands fit in LDS and there are enough tiles to
+  // fill the device (SANA_OUT_KERNEL=2 asks for the tile kernel).
+  p.out_kind = (bf && H <= 80 && out_persist_lds_bytes(H) <= kMaxLds &&
+                (int64_t)B * ((N + 15) / 16) >= 2 * p.num_cus && env_int("SANA_OUT_KERNEL", kOutPersist) != kOutTile)
+                   ? kOutPersist
+                   : kOutTile;
   const size_t BH = (size_t)B * H;
   size_t off = 0;
   p.off_rk = off;   off = align_up(off + (norm ? (size_t)B * N * 4 : 0), 256);

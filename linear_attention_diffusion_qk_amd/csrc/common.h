@@ -55,6 +55,17 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Raw buffer resource over [base, base + bytes) (gfx9 descriptor word 3 for untyped 32-bit access).
+// A buffer store whose byte offset is not below `bytes` is discarded by the hardware range check, so
+// masked lanes can take kOutOfRange instead of a branch around the store.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
 __device__ __forceinline__ f32x4 loadf4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
 // Sum over the 4 lanes {l, l^16, l^32, l^48} (the four 16-lane groups of a wave64).

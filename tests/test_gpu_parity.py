@@ -3,6 +3,8 @@
 Gates: max |O_gpu - O_oracle| <= 1e-5 max|V| (fp32 I/O) and <= 2e-2 max|V| (bf16 I/O), plus the
 scale-aware bound relative to max |O_oracle| in parity_util.SCALE_BOUND.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -146,3 +148,56 @@ def test_rejects_bad_arguments_without_enqueueing(gpu_lib):
     with pytest.raises(gpu_lib.SanaError) as e:
         gpu_lib.sana_linear_attn_fwd(q, k, v, gq, gk, 1, 8, 70, 32, 1e-6, q)  # out aliases q
     assert e.value.status == 1
+
+
+def _with_env(name, value, fn):
+    old = os.environ.get(name)
+    os.environ[name] = value
+    try:
+        return fn()
+    finally:
+        if old is None:
+            del os.environ[name]
+        else:
+            os.environ[name] = old
+
+
+def _mixed_scale_rows(seed, B, N, H, rows):
+    """bf16 inputs where some query rows carry tiny values (1e-12) on the first ten heads only: for those
+    heads the eps / r_q term dominates the denominator, and r_q comes from the other heads' channels."""
+    inp = gen_attn(seed, B, N, H=H, dtype="bf16")
+    for b, n in rows:
+        inp.q[b, n, : 10 * 32] *= np.float32(1e-12)
+    from synth.gen import bf16_round
+    inp.q[:] = bf16_round(inp.q)
+    return inp
+
+
+def _rowwise_check(o, o_ref, rows, H, label):
+    """Relative check per (row, head) block: the gates relative to max|V| would not see these rows."""
+    og = o.float().cpu().numpy()
+    for b, n in rows:
+        for h in range(H):
+            ref = o_ref[b, n, 32 * h: 32 * h + 32]
+            got = og[b, n, 32 * h: 32 * h + 32]
+            scale = np.abs(ref).max()
+            err = np.abs(got - ref).max()
+            assert err <= 1e-2 * scale + 1e-30, f"{label}: row {b},{n} head {h}: err {err:.3e} vs scale {scale:.3e}"
+
+
+@pytest.mark.parametrize("kind", ["1", "2"])
+def test_output_kernels_agree_with_oracle(gpu_lib, kind):
+    """Persistent (1) and tile (2) output kernels on the same inputs."""
+    inp = gen_attn(41, 2, 2100, dtype="bf16")
+    o = _with_env("SANA_OUT_KERNEL", kind, lambda: run_attn(gpu_lib, inp))
+    check(o, oracle_out(inp), inp.v, "bf16", f"out kernel {kind}")
+
+
+@pytest.mark.parametrize("kind", ["1", "2"])
+def test_mixed_scale_query_rows(gpu_lib, kind):
+    rows = [(0, 3), (0, 64), (1, 100), (1, 4000)]
+    inp = _mixed_scale_rows(42, 2, 4100, 70, rows)
+    o_ref = oracle_out(inp)
+    o = _with_env("SANA_OUT_KERNEL", kind, lambda: run_attn(gpu_lib, inp))
+    check(o, o_ref, inp.v, "bf16", "mixed-scale rows")
+    _rowwise_check(o, o_ref, rows, 70, "mixed-scale rows")
