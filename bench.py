@@ -146,8 +146,9 @@ def kernel_times(inputs: Inputs, sanala, reps: int = 20):
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
-def cpu_baseline(inputs: Inputs, min_seconds: float = 10.0, max_reps: int = 20):
-    """The fp64 oracle as it stands, on the same host arrays, repeated until >= min_seconds of CPU work."""
+def cpu_baseline(inputs: Inputs, min_seconds: float = 12.0, max_reps: int = 200):
+    """The fp64 oracle as it stands, on the same host arrays, repeated until >= min_seconds of CPU work
+    (about 12-15 s on the 4K workload)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info

@@ -413,20 +413,21 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
 
   u32x4 qa[2 * PPW], qb[2 * PPW];
   {
-    // The first sample's operands are requested ahead of the first Q tile so that the wait below
-    // covers only them (vmcnt retires in issue order): the tile's loads stay in flight.
+    // Each wave copies the first sample's operands of its own heads (the only ones it reads until the
+    // sample changes) ahead of its first Q tile, so the wait below covers only them (vmcnt retires in
+    // issue order) and needs no block-wide barrier; the tile's loads stay in flight.
     const int64_t b0 = tau0 / tiles_per_sample;
-    dma_to_lds(Sop + b0 * H * kOpPerHead, Ss, H * kOpPerHead * 2, w, NW, lane);
-    dma_to_lds(zop + b0 * H * kZopPerHead, Zs, H * kZopPerHead * 2, w, NW, lane);
-    dma_to_lds(gsg, Gs, H * kSgnPerHead * 4, w, NW, lane);
+    const int hb = min(H, 2 * w * PPW), he = min(H, 2 * (w + 1) * PPW);
+    if (he > hb) {
+      dma_to_lds(Sop + (b0 * H + hb) * kOpPerHead, Ss + hb * kOpPerHead, (he - hb) * kOpPerHead * 2, 0, 1, lane);
+      dma_to_lds(zop + (b0 * H + hb) * kZopPerHead, Zs + hb * kZopPerHead, (he - hb) * kZopPerHead * 2, 0, 1, lane);
+      dma_to_lds(gsg + hb * kSgnPerHead, Gs + hb * kSgnPerHead, (he - hb) * kSgnPerHead * 4, 0, 1, lane);
+    }
     __asm__ __volatile__("" ::: "memory");
     load_tile(tau0, qa);
     __asm__ __volatile__("" ::: "memory");
     static_assert(2 * PPW <= 15, "vmcnt immediate holds 4 low bits here");
     __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * PPW));  // vmcnt <= 2*PPW, expcnt/lgkmcnt not waited on
-    // A bare s_barrier: __syncthreads() would also wait for the tile's loads.
-    __asm__ __volatile__("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
     __asm__ __volatile__("" ::: "memory");
     cur_b = b0;
   }
