@@ -29,23 +29,30 @@ struct AttnPlan {
 AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm);
 
 // q is read with row stride ldq, k and v with ldkv, out written with ldo (all in elements).
+// k_ssq (bf16 path only, optional): per-row partial sums of squares of K in k_parts column panels,
+// row-major [B*N][k_parts] (from the projection epilogue); when given, r_k is formed from them and the
+// row-statistics pass over K is skipped.
 hipError_t launch_attn(const AttnPlan& p, const void* q, int64_t ldq, const void* k, const void* v, int64_t ldkv,
                        const float* gq, const float* gk, float eps, void* out, int64_t ldo, void* ws,
-                       hipStream_t stream);
+                       hipStream_t stream, const float* k_ssq = nullptr, int k_parts = 0);
 
 hipError_t launch_attn_f32(const AttnPlan& p, const float* q, int64_t ldq, const float* k, const float* v,
                            int64_t ldkv, const float* gq, const float* gk, float eps, float* out, int64_t ldo,
                            void* ws, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnPlan& p, const uint16_t* q, int64_t ldq, const uint16_t* k, const uint16_t* v,
                             int64_t ldkv, const float* gq, const float* gk, float eps, uint16_t* out, int64_t ldo,
-                            void* ws, int num_cus, hipStream_t stream);
+                            void* ws, int num_cus, hipStream_t stream, const float* k_ssq, int k_parts);
 size_t out_persist_lds_bytes(int H);
 size_t bf16_operand_bytes(int64_t BH, int H);
 
 int max_heads();
 
-// qkv[M, 3C] = x[M, C] @ w[C, 3C], bf16 in / bf16 out (fp32 accumulation).
-hipError_t launch_qkv_gemm(const uint16_t* x, const uint16_t* w, uint16_t* qkv, int64_t M, int C, hipStream_t stream);
+// qkv[M, 3C] = x[M, C] @ w[C, 3C], bf16 in / bf16 out (fp32 accumulation).  With k_ssq set, the blocks
+// whose columns overlap the K block [C, 2C) also write, per row, the sum of squares of the bf16 outputs
+// they hold in that block: k_ssq[m * qkv_gemm_k_parts(C) + j] for the j-th such column panel.
+hipError_t launch_qkv_gemm(const uint16_t* x, const uint16_t* w, uint16_t* qkv, int64_t M, int C, hipStream_t stream,
+                           float* k_ssq = nullptr);
+int qkv_gemm_k_parts(int C);
 
 // Measurement hooks (no-ops unless timing is enabled on the calling host thread): an event pair is
 // recorded on `s` around each kernel launch.

@@ -517,7 +517,7 @@ constexpr int kPersistPPW = 5;  // head pairs per wave in the persistent output 
 
 hipError_t launch_attn_bf16(const AttnPlan& p, const uint16_t* q, int64_t ldq, const uint16_t* k, const uint16_t* v,
                             int64_t ldkv, const float* gq, const float* gk, float eps, uint16_t* out, int64_t ldo,
-                            void* ws, int num_cus, hipStream_t stream) {
+                            void* ws, int num_cus, hipStream_t stream, const float* k_ssq, int k_parts) {
   char* base = static_cast<char*>(ws);
   float* r_k = reinterpret_cast<float*>(base + p.off_rk);
   float* part = reinterpret_cast<float*>(base + p.off_part);
@@ -529,7 +529,11 @@ hipError_t launch_attn_bf16(const AttnPlan& p, const uint16_t* q, int64_t ldq, c
   const int64_t BH = (int64_t)B * H;
   const unsigned rs_blocks = (unsigned)((rows + 3) / 4);
 
-  if (p.norm)
+  const float inv_C = 1.0f / (float)C;
+  if (p.norm && k_ssq)
+    SANA_LAUNCH("rowfinish_k", rowfinish_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(
+                                   k_ssq, k_parts, rows, inv_C, eps, r_k));
+  else if (p.norm)
     SANA_LAUNCH("rowstats_k", rowstats_kernel<uint16_t><<<rs_blocks, 256, 0, stream>>>(k, ldkv, rows, C, eps, r_k));
   const dim3 grid(p.NC, (H + 1) / 2, B);
   if (p.norm)
@@ -548,7 +552,6 @@ hipError_t launch_attn_bf16(const AttnPlan& p, const uint16_t* q, int64_t ldq, c
                   kv_reduce_bf16<false><<<blocks, 256, 0, stream>>>(part, p.NC, H, BH, nullptr, nullptr, Sop, zop, gsg));
   }
 
-  const float inv_C = 1.0f / (float)C;
   if (p.out_kind == kOutPersist) {
     const int64_t tiles = (int64_t)B * ((N + 15) / 16);
     const int blocks = (int)std::min<int64_t>(num_cus, tiles);

@@ -71,13 +71,13 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
 
 hipError_t launch_attn(const AttnPlan& p, const void* q, int64_t ldq, const void* k, const void* v, int64_t ldkv,
                        const float* gq, const float* gk, float eps, void* out, int64_t ldo, void* ws,
-                       hipStream_t stream) {
+                       hipStream_t stream, const float* k_ssq, int k_parts) {
   if (p.dtype == kDtypeF32)
     return launch_attn_f32(p, static_cast<const float*>(q), ldq, static_cast<const float*>(k),
                            static_cast<const float*>(v), ldkv, gq, gk, eps, static_cast<float*>(out), ldo, ws, stream);
   return launch_attn_bf16(p, static_cast<const uint16_t*>(q), ldq, static_cast<const uint16_t*>(k),
                           static_cast<const uint16_t*>(v), ldkv, gq, gk, eps, static_cast<uint16_t*>(out), ldo, ws,
-                          p.num_cus, stream);
+                          p.num_cus, stream, k_ssq, k_parts);
 }
 
 }  // namespace sanala

@@ -113,7 +113,8 @@ __device__ __forceinline__ void mma(const Ops& op, int s, f32x16 (&acc)[3][4]) {
 __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ w,
                                                             uint16_t* __restrict__ y, int M, int K, int NO,
-                                                            int mblocks, int nblocks, int slab) {
+                                                            int mblocks, int nblocks, int slab,
+                                                            float* __restrict__ k_ssq, int k_parts) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
 
@@ -212,6 +213,14 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const uint16_t* __re
   wait_vm<0>();  // no load into LDS outlives the block
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the last (unused) operand reads have returned
 
+  // Stores, and (k_ssq) per-row sums of squares of the stored bf16 values that fall in the K block
+  // [K, 2K) (K = C here).  A 32-column tile lies wholly inside or outside that block (C is a multiple of
+  // 32), and v_dot2_f32_bf16 squares the packed pairs being stored; the lane sum (tiles, then
+  // quads in order) is combined with the other column half of the wave (lanes l, l + 32) and then with
+  // the other wave of the same rows through LDS, always in that order.
+  const int nb_k0 = K / BN;
+  const bool row_ssq = k_ssq && nb >= nb_k0 && nb <= (2 * K - 1) / BN;
+  float ss[4] = {0.f, 0.f, 0.f, 0.f};
   // acc[nt][mt] lane l, register 4q + i: row m = 32 mt + l % 32, column n = 32 nt + 8q + 4(l / 32) + i.
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
@@ -219,28 +228,48 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const uint16_t* __re
     if (m >= M) continue;
 #pragma unroll
     for (int nt = 0; nt < 3; ++nt) {
+      const int ntile = n0 + 96 * wn + 32 * nt;
+      const bool in_k = row_ssq && ntile >= K && ntile < 2 * K;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + 96 * wn + 32 * nt + 8 * q + 4 * (lane >> 5);
+        const int n = ntile + 8 * q + 4 * (lane >> 5);
+        const f32x16& a = acc[nt][mt];
+        const uint32_t p0 = cvt_pk_bf16(a[4 * q], a[4 * q + 1]);
+        const uint32_t p1 = cvt_pk_bf16(a[4 * q + 2], a[4 * q + 3]);
         if (n < NO) {
-          const f32x16& a = acc[nt][mt];
           uint32_t* dst = reinterpret_cast<uint32_t*>(y + (int64_t)m * NO + n);
-          dst[0] = cvt_pk_bf16(a[4 * q], a[4 * q + 1]);
-          dst[1] = cvt_pk_bf16(a[4 * q + 2], a[4 * q + 3]);
+          dst[0] = p0;
+          dst[1] = p1;
         }
+        if (in_k) ss[mt] = dot2_bf16(p1, p1, dot2_bf16(p0, p0, ss[mt]));
       }
     }
   }
+  if (row_ssq) {
+    __syncthreads();  // the stage buffers are free
+    float* red = reinterpret_cast<float*>(g_stage0);  // [2 column halves of the block][256 rows]
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const float t = ss[mt] + __shfl_xor(ss[mt], 32);
+      if (lane < 32) red[wn * BM + 128 * wm + 32 * mt + lane] = t;
+    }
+    __syncthreads();
+    const int m = m0 + tid;
+    if (m < M) k_ssq[(int64_t)m * k_parts + (nb - nb_k0)] = red[tid] + red[BM + tid];
+  }
 }
 
-hipError_t launch_qkv_gemm(const uint16_t* x, const uint16_t* w, uint16_t* qkv, int64_t M, int C, hipStream_t stream) {
+int qkv_gemm_k_parts(int C) { return (2 * C - 1) / BN - C / BN + 1; }
+
+hipError_t launch_qkv_gemm(const uint16_t* x, const uint16_t* w, uint16_t* qkv, int64_t M, int C, hipStream_t stream,
+                           float* k_ssq) {
   const int NO = 3 * C;
   if (C % BK != 0 || M > (1LL << 30)) return hipErrorInvalidValue;
   const int mblocks = (int)((M + BM - 1) / BM), nblocks = (NO + BN - 1) / BN;
   const int slab = mblocks >= 8 ? (mblocks + 7) / 8 : 0;
   const int64_t blocks = slab > 0 ? (int64_t)8 * slab * nblocks : (int64_t)mblocks * nblocks;
   SANA_LAUNCH("qkv_gemm", qkv_gemm_kernel<<<(unsigned)blocks, kThreads, 0, stream>>>(
-                              x, w, qkv, (int)M, C, NO, mblocks, nblocks, slab));
+                              x, w, qkv, (int)M, C, NO, mblocks, nblocks, slab, k_ssq, qkv_gemm_k_parts(C)));
   return hipGetLastError();
 }
 

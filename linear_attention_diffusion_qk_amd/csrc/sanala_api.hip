@@ -164,15 +164,20 @@ extern "C" sana_status_t sana_qkv_linear_attn_fwd(const void* x, const void* Wqk
   g_timing.count = 0;
   const bool norm = gq != nullptr;
   const sanala::AttnPlan plan = sanala::plan_attn(B, N, H, sanala::kDtypeBf16, norm);
+  // With the QK-Norm on, the projection's epilogue also leaves per-row partial sums of squares of K,
+  // which replace the attention's row-statistics pass over K.
   const size_t qkv_bytes = ((size_t)M * 3 * C * 2 + 255) / 256 * 256;
+  const int k_parts = norm ? sanala::qkv_gemm_k_parts((int)C) : 0;
+  const size_t ssq_bytes = ((size_t)M * k_parts * 4 + 255) / 256 * 256;
   void* ws = nullptr;
-  if (hipMallocAsync(&ws, qkv_bytes + plan.ws_bytes, stream) != hipSuccess) return SANA_ERR_HIP;
+  if (hipMallocAsync(&ws, qkv_bytes + ssq_bytes + plan.ws_bytes, stream) != hipSuccess) return SANA_ERR_HIP;
   uint16_t* qkv = static_cast<uint16_t*>(ws);
+  float* k_ssq = norm ? reinterpret_cast<float*>(static_cast<char*>(ws) + qkv_bytes) : nullptr;
   hipError_t e = sanala::launch_qkv_gemm(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(Wqkv), qkv, M,
-                                         (int)C, stream);
+                                         (int)C, stream, k_ssq);
   if (e == hipSuccess)
     e = sanala::launch_attn(plan, qkv, 3 * C, qkv + C, qkv + 2 * C, 3 * C, gq, gk, eps, out, C,
-                            static_cast<char*>(ws) + qkv_bytes, stream);
+                            static_cast<char*>(ws) + qkv_bytes + ssq_bytes, stream, k_ssq, k_parts);
   const hipError_t ef = hipFreeAsync(ws, stream);
   return (e == hipSuccess && ef == hipSuccess) ? SANA_OK : SANA_ERR_HIP;
 }
