@@ -201,3 +201,26 @@ def test_mixed_scale_query_rows(gpu_lib, kind):
     o = _with_env("SANA_OUT_KERNEL", kind, lambda: run_attn(gpu_lib, inp))
     check(o, o_ref, inp.v, "bf16", "mixed-scale rows")
     _rowwise_check(o, o_ref, rows, 70, "mixed-scale rows")
+
+
+def _sampled_rows_check(o, inp, label, rows_per_sample=96, seed=0):
+    """Oracle on sampled output rows (the first and last token always included): the state from all
+    tokens, the output for the sampled rows only."""
+    rng = np.random.default_rng(seed)
+    N = inp.N
+    phik = oracle.feature_map(inp.k, inp.gk, inp.eps)
+    S, z = oracle.kv_state(phik, inp.v, inp.H, inp.D)
+    idx = np.unique(np.concatenate([rng.choice(N, size=min(rows_per_sample, N), replace=False), [0, N - 1]]))
+    phiq = oracle.feature_map(inp.q[:, idx], inp.gq, inp.eps)
+    o_ref = oracle.attend(phiq, S, z, inp.eps, inp.H, inp.D)
+    check(o[:, torch.from_numpy(idx).to(o.device)], o_ref, inp.v, inp.dtype, label)
+
+
+@pytest.mark.parametrize("B,N", [(1, 65536), (3, 20011)])
+def test_long_sequences_sampled_rows(gpu_lib, B, N):
+    """Four times the 4K token count (several hundred MB per tensor: 64-bit offsets, many chunks per
+    sample) and a ragged batch whose output tiles cross sample boundaries."""
+    inp = gen_attn(45 + N, B, N, dtype="bf16")
+    o = run_attn(gpu_lib, inp)
+    assert not torch.isnan(o).any()
+    _sampled_rows_check(o, inp, f"B={B} N={N}")

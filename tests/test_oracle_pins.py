@@ -380,3 +380,27 @@ def test_denominator_leaves_fp16_range_at_4k():
     S, z = oracle.kv_state(oracle.feature_map(k, g, eps), rng.standard_normal((1, N, H * D)), H, D)
     den = pq[0] @ z[0, 0]
     assert np.median(den) > 65504.0
+
+
+def test_fp16_accumulated_state_overflows_without_norm():
+    """The SANA notes report FP16 overflow (NaN) in linear attention without QK-Norm.  With the 4K
+    workload's keys (sd 30, 1% of rows x100) and the norm off, z = sum_j ReLU(k_j) reaches ~4.6e5: a
+    running sum kept in binary16 overflows to inf and the output of Eq. (1) becomes NaN, while the
+    fp64 state of the oracle (and the fp32 state of the GPU path) stays finite."""
+    from synth import gen_attn
+    inp = gen_attn(4, 1, 16384, H=1, dtype="bf16", k_scale=30.0, outlier_frac=0.01, norm=False)
+    k0 = inp.k[0].astype(np.float64)
+    v0 = inp.v[0].astype(np.float64)
+    q0 = inp.q[0].astype(np.float64)
+    phik = np.maximum(k0, 0.0)
+    z64 = phik.sum(axis=0)
+    assert z64.max() > 65504.0 and np.isfinite(z64).all()
+    z16 = np.cumsum(phik.astype(np.float16), axis=0, dtype=np.float16)[-1]
+    assert np.isinf(z16).any()
+    S16 = (phik.astype(np.float16).T @ v0.astype(np.float16)).astype(np.float16)
+    phiq = np.maximum(q0, 0.0).astype(np.float16)
+    with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
+        o16 = (phiq @ S16) / (phiq @ z16 + np.float16(inp.eps))[:, None]
+    assert np.isnan(o16).any() or not np.isfinite(o16).all()
+    o64 = oracle.linear_attn(inp.q, inp.k, inp.v, None, None, 1, 32, inp.eps)
+    assert np.isfinite(o64).all()
