@@ -47,7 +47,10 @@ typedef enum {
 
 typedef enum {
   SANA_F32 = 0,  /* fp32 storage, fp32 arithmetic */
-  SANA_BF16 = 1  /* bf16 storage; fp32 accumulation; bf16 MFMA operands; outputs rounded to nearest even */
+  SANA_BF16 = 1, /* bf16 storage; fp32 accumulation; bf16 MFMA operands; outputs rounded to nearest even */
+  SANA_F16 = 2   /* IEEE binary16 storage; fp32 sums of squares and KV state (fp16 MFMA operands for the
+                    state, bf16 operands for the output contraction, whose state values can exceed
+                    the binary16 range); outputs rounded to nearest even (overflow gives +-inf) */
 } sana_dtype_t;
 
 /*
@@ -59,7 +62,7 @@ typedef enum {
  *   eps      finite, >= 0 (SANA uses 1e-6).
  *   out      device, [B, N, H*D] of `dtype`, contiguous, 16-byte aligned; fully overwritten.
  *   stream   HIP stream the work is enqueued on (0 = the null stream).
- *   dtype    SANA_F32 or SANA_BF16 (storage type of q, k, v and out).
+ *   dtype    SANA_F32, SANA_BF16 or SANA_F16 (storage type of q, k, v and out).
  *
  * Returns SANA_OK once the work is enqueued, or an error code with nothing enqueued.
  */

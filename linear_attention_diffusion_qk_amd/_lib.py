@@ -18,6 +18,7 @@ SANA_ERR_MISALIGNED = 3
 SANA_ERR_HIP = 4
 SANA_F32 = 0
 SANA_BF16 = 1
+SANA_F16 = 2
 
 # Every symbol include/sanala.h declares.
 EXPORTS = ("sana_linear_attn_fwd", "sana_qkv_linear_attn_fwd", "sana_status_string",

@@ -12,7 +12,7 @@ import torch
 from . import _lib
 from ._lib import SanaError
 
-_DTYPES = {torch.float32: _lib.SANA_F32, torch.bfloat16: _lib.SANA_BF16}
+_DTYPES = {torch.float32: _lib.SANA_F32, torch.bfloat16: _lib.SANA_BF16, torch.float16: _lib.SANA_F16}
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -61,11 +61,11 @@ def sana_qkv_linear_attn_fwd(x, Wqkv, gq, gk, B: int, N: int, H: int, D: int, ep
 def linear_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gq: Optional[torch.Tensor],
                 gk: Optional[torch.Tensor], H: int, D: int = 32, eps: float = 1e-6,
                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """O = phi(Q) S / (phi(Q).z + eps) for q, k, v of shape [B, N, H*D] (fp32 or bf16)."""
+    """O = phi(Q) S / (phi(Q).z + eps) for q, k, v of shape [B, N, H*D] (fp32, bf16 or binary16)."""
     if q.dim() != 3 or q.shape != k.shape or q.shape != v.shape:
         raise ValueError("q, k, v must share one [B, N, H*D] shape")
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must all be float32 or all bfloat16")
+        raise ValueError("q, k, v must all be float32, all bfloat16 or all float16")
     B, N, C = q.shape
     if C != H * D:
         raise ValueError(f"last dim {C} != H*D = {H}*{D}")

@@ -11,6 +11,7 @@ namespace sanala {
 constexpr int kHeadDim = 32;  // D: the only head size with kernels
 constexpr int kDtypeF32 = 0;
 constexpr int kDtypeBf16 = 1;
+constexpr int kDtypeF16 = 2;
 constexpr int kOutPersist = 1;  // bf16 output: one block per CU, all heads, operands in LDS
 constexpr int kOutTile = 2;     // bf16 output: 16-token tiles over all heads, operands from global memory
 
@@ -39,6 +40,7 @@ hipError_t launch_attn(const AttnPlan& p, const void* q, int64_t ldq, const void
 hipError_t launch_attn_f32(const AttnPlan& p, const float* q, int64_t ldq, const float* k, const float* v,
                            int64_t ldkv, const float* gq, const float* gk, float eps, float* out, int64_t ldo,
                            void* ws, hipStream_t stream);
+// 16-bit storage (bf16 or binary16, p.dtype).
 hipError_t launch_attn_bf16(const AttnPlan& p, const uint16_t* q, int64_t ldq, const uint16_t* k, const uint16_t* v,
                             int64_t ldkv, const float* gq, const float* gk, float eps, uint16_t* out, int64_t ldo,
                             void* ws, int num_cus, hipStream_t stream, const float* k_ssq, int k_parts);

@@ -77,7 +77,7 @@ __device__ __forceinline__ void emit_state(int64_t bh, int h, int i, float s, co
 // 16-token step), B[t][e] = v_t,e; accumulator lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4,
 // column l%32.  A second MFMA against an all-ones B gives z~ in every column.
 // ---------------------------------------------------------------------------------------------
-template <bool NORM>
+template <bool NORM, bool F16>
 __global__ __launch_bounds__(256) void kv_state_bf16(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                      int64_t ld, const float* __restrict__ r_k,
                                                      const float* __restrict__ gq, const float* __restrict__ gk,
@@ -102,7 +102,8 @@ __global__ __launch_bounds__(256) void kv_state_bf16(const uint16_t* __restrict_
   const int hcol = min(h0 + hh, H - 1) * kHeadDim + d;
   const uint32_t sgn = (NORM && gk[hcol] < 0.f) ? 0x80008000u : 0u;  // flips both tokens of a pair
   const int64_t row0 = (int64_t)b * N;
-  const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  constexpr uint32_t kOne2 = F16 ? 0x3c003c00u : 0x3f803f80u;  // two 1.0 values
+  const u32x4 ones = {kOne2, kOne2, kOne2, kOne2};
 
   u32x4 pk[2], pv[2];
   float pr = 1.f;
@@ -160,11 +161,17 @@ __global__ __launch_bounds__(256) void kv_state_bf16(const uint16_t* __restrict_
         const float rr[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          aw[u] = cvt_pk_bf16(bf16_lo(aw[u]) * rr[2 * u], bf16_hi(aw[u]) * rr[2 * u + 1]);
+          aw[u] = cvt_pk_h<F16>(h_lo<F16>(aw[u]) * rr[2 * u], h_hi<F16>(aw[u]) * rr[2 * u + 1]);
       }
-      const bf16x8 A = as_bf16x8(u32x4{aw[0], aw[1], aw[2], aw[3]});
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, as_bf16x8(u32x4{bw[0], bw[1], bw[2], bw[3]}), acc, 0, 0, 0);
-      accz = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, as_bf16x8(ones), accz, 0, 0, 0);
+      const u32x4 A = {aw[0], aw[1], aw[2], aw[3]};
+      const u32x4 Bv = {bw[0], bw[1], bw[2], bw[3]};
+      if constexpr (F16) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(A), as_f16x8(Bv), acc, 0, 0, 0);
+        accz = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(A), as_f16x8(ones), accz, 0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A), as_bf16x8(Bv), acc, 0, 0, 0);
+        accz = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A), as_bf16x8(ones), accz, 0, 0, 0);
+      }
     }
     __syncthreads();
   }
@@ -241,11 +248,15 @@ __global__ __launch_bounds__(256) void kv_reduce_bf16(const float* __restrict__ 
 // S'^T; zh/zl: z' hi and lo at those dims; epsr = eps / r_q of token t; even_row: lane index even.
 // Returns output channels 8kg..8kg+7 of token t as bf16 (1/den by v_rcp_f32, 1 ulp).
 // ---------------------------------------------------------------------------------------------
+template <bool F16>
 __device__ __forceinline__ u32x4 head_out(u32x4 qv, u32x4 sg, bf16x8 a0, bf16x8 a1, u32x4 zh, u32x4 zl, float epsr,
                                           bool even_row, float* den = nullptr) {
   u32x4 psi;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) psi[u] = relu_bf16x2(qv[u] ^ sg[u]);
+  for (int u = 0; u < 4; ++u) {
+    psi[u] = relu_bf16x2(qv[u] ^ sg[u]);
+    if (F16) psi[u] = cvt_pk_bf16(f16_lo(psi[u]), f16_hi(psi[u]));  // the contraction runs on bf16 operands
+  }
   const bf16x8 Bq = as_bf16x8(psi);
   // z-block of S'^T: rows with even index hold z' hi, odd rows z' lo, so result registers 0 and 1 of
   // every lane are psi.z'_hi and psi.z'_lo of its token, and their sum is the denominator.
@@ -258,8 +269,8 @@ __device__ __forceinline__ u32x4 head_out(u32x4 qv, u32x4 sg, bf16x8 a0, bf16x8 
   const float d = oz[0] + oz[1];
   if (den) *den = d;
   const float inv = __builtin_amdgcn_rcpf(d + epsr);
-  return u32x4{cvt_pk_bf16(o0[0] * inv, o0[1] * inv), cvt_pk_bf16(o0[2] * inv, o0[3] * inv),
-               cvt_pk_bf16(o1[0] * inv, o1[1] * inv), cvt_pk_bf16(o1[2] * inv, o1[3] * inv)};
+  return u32x4{cvt_pk_h<F16>(o0[0] * inv, o0[1] * inv), cvt_pk_h<F16>(o0[2] * inv, o0[3] * inv),
+               cvt_pk_h<F16>(o1[0] * inv, o1[1] * inv), cvt_pk_h<F16>(o1[2] * inv, o1[3] * inv)};
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -300,7 +311,7 @@ __device__ __forceinline__ u32x4 swap_halves(u32x4 old, u32x4 src) {
 // consumes the current one; nothing else in the tile loop reads global memory.  The row sums of
 // squares are combined across waves through LDS in a fixed order.
 // ---------------------------------------------------------------------------------------------
-template <int PPW, bool NORM>
+template <int PPW, bool NORM, bool F16>
 __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restrict__ q, int64_t ldq,
                                                         const uint32_t* __restrict__ gsg,
                                                         const uint16_t* __restrict__ Sop,
@@ -368,7 +379,7 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
       for (int i = 0; i < 2 * PPW; ++i)
         if (2 * w * PPW + i < H) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) ss = dot2_bf16(bq[i][u], bq[i][u], ss);
+          for (int u = 0; u < 4; ++u) ss = dot2_h<F16>(bq[i][u], bq[i][u], ss);
         }
       ss = sum_over_lane_groups(ss);
       float* sb = ssq + (tau & 1) * 8 * 16;
@@ -394,7 +405,7 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
           const int h = min(h0 + j, H - 1);
           const uint16_t* sh = Ss + h * kOpPerHead + lane * 8;
           const uint16_t* zh = Zs + h * kZopPerHead + kg * 8;
-          o[j] = head_out(bq[2 * i + j], *reinterpret_cast<const u32x4*>(Gs + h * kSgnPerHead + kg * 4),
+          o[j] = head_out<F16>(bq[2 * i + j], *reinterpret_cast<const u32x4*>(Gs + h * kSgnPerHead + kg * 4),
                           as_bf16x8(*reinterpret_cast<const u32x4*>(sh)),
                           as_bf16x8(*reinterpret_cast<const u32x4*>(sh + 512)), *reinterpret_cast<const u32x4*>(zh),
                           *reinterpret_cast<const u32x4*>(zh + kHeadDim), epsr, (lane & 1) == 0);
@@ -450,7 +461,7 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
 // [g0 + w*HPW, g0 + w*HPW + HPW).  PRE_R = false: the block covers all H heads and forms r_q from the
 // Q rows it holds; PRE_R = true: r_q comes from a row-statistics pass (H > 4*HPW).
 // ---------------------------------------------------------------------------------------------
-template <int HPW, bool NORM, bool PRE_R>
+template <int HPW, bool NORM, bool PRE_R, bool F16>
 __global__ __launch_bounds__(256) void out_bf16(const uint16_t* __restrict__ q, int64_t ldq,
                                                 const uint32_t* __restrict__ gsg, const uint16_t* __restrict__ Sop,
                                                 const uint16_t* __restrict__ zop, const float* __restrict__ r_q, int N,
@@ -478,7 +489,7 @@ __global__ __launch_bounds__(256) void out_bf16(const uint16_t* __restrict__ q, 
     for (int i = 0; i < HPW; ++i)
       if (i < hcnt) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) ss = dot2_bf16(qr[i][u], qr[i][u], ss);
+        for (int u = 0; u < 4; ++u) ss = dot2_h<F16>(qr[i][u], qr[i][u], ss);
       }
     ss = sum_over_lane_groups(ss);
     if (kg == 0) ssq[w][t] = ss;
@@ -494,7 +505,7 @@ __global__ __launch_bounds__(256) void out_bf16(const uint16_t* __restrict__ q, 
       const u32x4 sg = load16(gsg + h * kSgnPerHead + kg * 4);
       const uint16_t* sh = Sop + bh * kOpPerHead + lane * 8;
       const uint16_t* zh = zop + bh * kZopPerHead + kg * 8;
-      const u32x4 o = head_out(qr[i], sg, as_bf16x8(load16(sh)), as_bf16x8(load16(sh + 512)), load16(zh),
+      const u32x4 o = head_out<F16>(qr[i], sg, as_bf16x8(load16(sh)), as_bf16x8(load16(sh + 512)), load16(zh),
                                load16(zh + kHeadDim), epsr, (lane & 1) == 0);
       if (n < N) store16(out + (row0 + n) * ldo + h * kHeadDim + kg * 8, o);
     }
@@ -515,9 +526,11 @@ size_t bf16_operand_bytes(int64_t BH, int H) {
 
 constexpr int kPersistPPW = 5;  // head pairs per wave in the persistent output kernel (<= 8 waves: H <= 80)
 
-hipError_t launch_attn_bf16(const AttnPlan& p, const uint16_t* q, int64_t ldq, const uint16_t* k, const uint16_t* v,
-                            int64_t ldkv, const float* gq, const float* gk, float eps, uint16_t* out, int64_t ldo,
-                            void* ws, int num_cus, hipStream_t stream, const float* k_ssq, int k_parts) {
+template <bool F16>
+static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t ldq, const uint16_t* k,
+                                 const uint16_t* v, int64_t ldkv, const float* gq, const float* gk, float eps,
+                                 uint16_t* out, int64_t ldo, void* ws, int num_cus, hipStream_t stream,
+                                 const float* k_ssq, int k_parts) {
   char* base = static_cast<char*>(ws);
   float* r_k = reinterpret_cast<float*>(base + p.off_rk);
   float* part = reinterpret_cast<float*>(base + p.off_part);
@@ -534,13 +547,13 @@ hipError_t launch_attn_bf16(const AttnPlan& p, const uint16_t* q, int64_t ldq, c
     SANA_LAUNCH("rowfinish_k", rowfinish_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(
                                    k_ssq, k_parts, rows, inv_C, eps, r_k));
   else if (p.norm)
-    SANA_LAUNCH("rowstats_k", rowstats_kernel<uint16_t><<<rs_blocks, 256, 0, stream>>>(k, ldkv, rows, C, eps, r_k));
+    SANA_LAUNCH("rowstats_k", rowstats_kernel<uint16_t, F16><<<rs_blocks, 256, 0, stream>>>(k, ldkv, rows, C, eps, r_k));
   const dim3 grid(p.NC, (H + 1) / 2, B);
   if (p.norm)
-    SANA_LAUNCH("kv_state", kv_state_bf16<true><<<grid, 256, 0, stream>>>(k, v, ldkv, r_k, gq, gk, N, H, p.Tc, p.NC,
+    SANA_LAUNCH("kv_state", kv_state_bf16<true, F16><<<grid, 256, 0, stream>>>(k, v, ldkv, r_k, gq, gk, N, H, p.Tc, p.NC,
                                                                           part, Sop, zop, gsg));
   else
-    SANA_LAUNCH("kv_state", kv_state_bf16<false><<<grid, 256, 0, stream>>>(k, v, ldkv, nullptr, nullptr, nullptr, N, H,
+    SANA_LAUNCH("kv_state", kv_state_bf16<false, F16><<<grid, 256, 0, stream>>>(k, v, ldkv, nullptr, nullptr, nullptr, N, H,
                                                                            p.Tc, p.NC, part, Sop, zop, gsg));
   if (p.NC > 1) {
     const unsigned blocks = (unsigned)((BH * kPartStride + 255) / 256);
@@ -559,19 +572,19 @@ hipError_t launch_attn_bf16(const AttnPlan& p, const uint16_t* q, int64_t ldq, c
     const int nblk = (int)((tiles + per - 1) / per);
     const size_t lds = out_persist_lds_bytes(H);
     const int nw = ((H + 1) / 2 + kPersistPPW - 1) / kPersistPPW;
-    static bool attr_set = false;
+    static bool attr_set = false;  // one flag per storage type
     if (!attr_set) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&out_persist_bf16<kPersistPPW, true>),
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&out_persist_bf16<kPersistPPW, true, F16>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&out_persist_bf16<kPersistPPW, false>),
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&out_persist_bf16<kPersistPPW, false, F16>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
       attr_set = true;
     }
     if (p.norm)
-      SANA_LAUNCH("out", out_persist_bf16<kPersistPPW, true><<<nblk, nw * 64, lds, stream>>>(
+      SANA_LAUNCH("out", out_persist_bf16<kPersistPPW, true, F16><<<nblk, nw * 64, lds, stream>>>(
                              q, ldq, gsg, Sop, zop, B, N, H, eps, inv_C, out, ldo, per));
     else
-      SANA_LAUNCH("out", out_persist_bf16<kPersistPPW, false><<<nblk, nw * 64, lds, stream>>>(
+      SANA_LAUNCH("out", out_persist_bf16<kPersistPPW, false, F16><<<nblk, nw * 64, lds, stream>>>(
                              q, ldq, gsg, Sop, zop, B, N, H, eps, inv_C, out, ldo, per));
     return hipGetLastError();
   }
@@ -579,24 +592,32 @@ hipError_t launch_attn_bf16(const AttnPlan& p, const uint16_t* q, int64_t ldq, c
   if (H <= 4 * HPW) {
     const dim3 ogrid((N + 15) / 16, B, 1);
     if (p.norm)
-      SANA_LAUNCH("out", out_bf16<HPW, true, false><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, nullptr, N, H, eps,
+      SANA_LAUNCH("out", out_bf16<HPW, true, false, F16><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, nullptr, N, H, eps,
                                                                               inv_C, out, ldo));
     else
-      SANA_LAUNCH("out", out_bf16<HPW, false, false><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, nullptr, N, H,
+      SANA_LAUNCH("out", out_bf16<HPW, false, false, F16><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, nullptr, N, H,
                                                                                eps, inv_C, out, ldo));
   } else {
     const dim3 ogrid((N + 15) / 16, B, (H + 4 * HPW - 1) / (4 * HPW));
     float* r_q = reinterpret_cast<float*>(base + p.off_rq);
     if (p.norm) {
-      SANA_LAUNCH("rowstats_q", rowstats_kernel<uint16_t><<<rs_blocks, 256, 0, stream>>>(q, ldq, rows, C, eps, r_q));
-      SANA_LAUNCH("out", out_bf16<HPW, true, true><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, r_q, N, H, eps,
+      SANA_LAUNCH("rowstats_q", rowstats_kernel<uint16_t, F16><<<rs_blocks, 256, 0, stream>>>(q, ldq, rows, C, eps, r_q));
+      SANA_LAUNCH("out", out_bf16<HPW, true, true, F16><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, r_q, N, H, eps,
                                                                              inv_C, out, ldo));
     } else {
-      SANA_LAUNCH("out", out_bf16<HPW, false, true><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, nullptr, N, H,
+      SANA_LAUNCH("out", out_bf16<HPW, false, true, F16><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, nullptr, N, H,
                                                                               eps, inv_C, out, ldo));
     }
   }
   return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16(const AttnPlan& p, const uint16_t* q, int64_t ldq, const uint16_t* k, const uint16_t* v,
+                            int64_t ldkv, const float* gq, const float* gk, float eps, uint16_t* out, int64_t ldo,
+                            void* ws, int num_cus, hipStream_t stream, const float* k_ssq, int k_parts) {
+  if (p.dtype == kDtypeF16)
+    return launch_attn_16<true>(p, q, ldq, k, v, ldkv, gq, gk, eps, out, ldo, ws, num_cus, stream, k_ssq, k_parts);
+  return launch_attn_16<false>(p, q, ldq, k, v, ldkv, gq, gk, eps, out, ldo, ws, num_cus, stream, k_ssq, k_parts);
 }
 
 }  // namespace sanala

@@ -38,7 +38,7 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
   p.dtype = dtype;
   p.norm = norm;
   p.num_cus = device_cus();
-  const bool bf = dtype == kDtypeBf16;
+  const bool bf = dtype != kDtypeF32;  // 16-bit storage: the bf16 / binary16 kernels
   // KV chunking: about 1024 blocks in total, chunks of at least 256 tokens (the partial state costs
   // 33/Tc of the K+V traffic), never more than the sequence.
   const int groups = bf ? (H + 1) / 2 : H;

@@ -13,6 +13,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 namespace sanala {
 
@@ -51,6 +53,30 @@ __device__ __forceinline__ uint32_t relu_bf16x2(uint32_t w) {
 // Two fp32 values to packed bf16 with the hardware converter (v_cvt_pk_bf16_f32, round to nearest even).
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+// IEEE binary16 counterparts (v_dot2_f32_f16, v_cvt_f32_f16, v_cvt_f16_f32 with round to nearest even).
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 w) { return __builtin_bit_cast(f16x8, w); }
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
+__device__ __forceinline__ uint32_t cvt_pk_f16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
+}
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
+}
+
+// The 16-bit storage type at compile time: F16 = IEEE binary16, else bf16.  Both keep the sign in the
+// top bit of each half, so the integer-max ReLU and the sign-mask XOR serve both.
+template <bool F16>
+__device__ __forceinline__ float h_lo(uint32_t w) { return F16 ? f16_lo(w) : bf16_lo(w); }
+template <bool F16>
+__device__ __forceinline__ float h_hi(uint32_t w) { return F16 ? f16_hi(w) : bf16_hi(w); }
+template <bool F16>
+__device__ __forceinline__ uint32_t cvt_pk_h(float lo, float hi) { return F16 ? cvt_pk_f16(lo, hi) : cvt_pk_bf16(lo, hi); }
+template <bool F16>
+__device__ __forceinline__ float dot2_h(uint32_t a, uint32_t b, float acc) {
+  return F16 ? dot2_f16(a, b, acc) : dot2_bf16(a, b, acc);
 }
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }

@@ -6,8 +6,8 @@
 namespace sanala {
 
 // r[row] = 1 / sqrt(mean_c x[row, c]^2 + eps) over all C channels of a token row (the QK-Norm
-// scale), one wave per row, 16-byte loads.  Rows are `ld` elements apart.
-template <typename T>
+// scale), one wave per row, 16-byte loads (16-bit T: bf16, or binary16 with F16).  Rows are `ld` elements apart.
+template <typename T, bool F16 = false>
 __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ x, int64_t ld, int64_t rows, int C,
                                                        float eps, float* __restrict__ r) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -20,7 +20,7 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ x, 
     const u32x4 w = load16(p + 16 * (int64_t)i);
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) ss = dot2_bf16(w[u], w[u], ss);
+      for (int u = 0; u < 4; ++u) ss = dot2_h<F16>(w[u], w[u], ss);
     } else {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {

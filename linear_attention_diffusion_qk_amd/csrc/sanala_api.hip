@@ -121,11 +121,11 @@ extern "C" sana_status_t sana_linear_attn_fwd(const void* q, const void* k, cons
                                               const float* gk, int B, int N, int H, int D, float eps, void* out,
                                               hipStream_t stream, sana_dtype_t dtype) {
   if (!q || !k || !v || !out) return SANA_ERR_INVALID_ARG;
-  if (dtype != SANA_F32 && dtype != SANA_BF16) return SANA_ERR_INVALID_ARG;
+  if (dtype != SANA_F32 && dtype != SANA_BF16 && dtype != SANA_F16) return SANA_ERR_INVALID_ARG;
   sana_status_t st = check_common(B, N, H, D, eps, gq, gk);
   if (st != SANA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SANA_ERR_MISALIGNED;
-  const size_t esz = dtype == SANA_BF16 ? 2 : 4;
+  const size_t esz = dtype == SANA_F32 ? 4 : 2;
   const size_t tbytes = (size_t)B * N * H * D * esz;
   if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, k, tbytes) || overlaps(out, tbytes, v, tbytes))
     return SANA_ERR_INVALID_ARG;
@@ -135,7 +135,7 @@ extern "C" sana_status_t sana_linear_attn_fwd(const void* q, const void* k, cons
   init_pool(dev);
   g_timing.count = 0;
   const bool norm = gq != nullptr;
-  const int dt = dtype == SANA_BF16 ? sanala::kDtypeBf16 : sanala::kDtypeF32;
+  const int dt = dtype == SANA_BF16 ? sanala::kDtypeBf16 : dtype == SANA_F16 ? sanala::kDtypeF16 : sanala::kDtypeF32;
   const sanala::AttnPlan plan = sanala::plan_attn(B, N, H, dt, norm);
   void* ws = nullptr;
   if (hipMallocAsync(&ws, plan.ws_bytes, stream) != hipSuccess) return SANA_ERR_HIP;

@@ -8,7 +8,8 @@ section, scale/resolution bullet), split here as 70 heads of 32.
 
 Every tensor is drawn in float64 from NumPy's PCG64 stream seeded with
 SeedSequence([config_id, sample, tensor_id]), cast to float32, and for bf16
-storage rounded to the nearest bf16 value (ties to even).  The arrays returned
+storage rounded to the nearest bf16 value (ties to even); for binary16 storage
+("f16") rounded to the nearest IEEE half value.  The arrays returned
 are float32 whose values are exactly representable in the storage type, so the
 GPU side can convert them without further rounding and the oracle can widen
 them to float64 exactly.
@@ -58,6 +59,8 @@ def _store(x64: np.ndarray, dtype: str) -> np.ndarray:
         return bf16_round(x32)
     if dtype == "f32":
         return x32
+    if dtype == "f16":
+        return x32.astype(np.float16).astype(np.float32)  # IEEE binary16, round to nearest even
     raise ValueError(f"unknown storage dtype {dtype!r}")
 
 

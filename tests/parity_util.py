@@ -6,14 +6,16 @@ import torch
 
 import oracle
 
-TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 # Gates on max |O_gpu - O_oracle| relative to max |V| for each storage type.
-GATE = {"f32": 1e-5, "bf16": 2e-2}
+GATE = {"f32": 1e-5, "bf16": 2e-2, "f16": 2e-2}
 # Scale-aware bounds relative to max |O_oracle|, derived from the arithmetic: fp32 I/O keeps every step
 # in fp32 (error a few ulp of the fp32 sums); bf16 I/O rounds phi(Q) to bf16 as an MFMA operand and the
-# output to bf16, 2^-9 relative each, so a few parts in 1e3 of the output scale.
-SCALE_BOUND = {"f32": 1e-5, "bf16": 1e-2}
+# output to bf16, 2^-9 relative each, so a few parts in 1e3 of the output scale.  binary16 I/O keeps
+# the same bf16 operands in the output contraction (its state values can exceed the binary16 range) and
+# rounds the output to binary16 (2^-11), so it takes the bf16 bounds.
+SCALE_BOUND = {"f32": 1e-5, "bf16": 1e-2, "f16": 1e-2}
 
 
 def dev(a: np.ndarray, dtype: str) -> torch.Tensor:

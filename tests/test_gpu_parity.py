@@ -1,6 +1,6 @@
 """GPU parity: the HIP path through the C-ABI against the fp64 oracle on the same seeded inputs.
 
-Gates: max |O_gpu - O_oracle| <= 1e-5 max|V| (fp32 I/O) and <= 2e-2 max|V| (bf16 I/O), plus the
+Gates: max |O_gpu - O_oracle| <= 1e-5 max|V| (fp32 I/O) and <= 2e-2 max|V| (bf16 and binary16 I/O), plus the
 scale-aware bound relative to max |O_oracle| in parity_util.SCALE_BOUND.
 """
 import os
@@ -16,7 +16,7 @@ from tests.parity_util import check, dev, gains_dev, oracle_out, run_attn
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("B,N", [(1, 1), (2, 17), (1, 64), (3, 100), (1, 333), (2, 1037)])
 def test_small_shapes_span_tiles_and_tails(gpu_lib, dtype, B, N):
     inp = gen_attn(1000 + N, B, N, dtype=dtype)
@@ -81,7 +81,7 @@ def test_structured_v(gpu_lib):
 
 def test_norm_off(gpu_lib):
     """QK-Norm off (both gains NULL): phi = ReLU, the SANA-1.0 form of Eq. (1)."""
-    for dtype in ("f32", "bf16"):
+    for dtype in ("f32", "bf16", "f16"):
         inp = gen_attn(32, 2, 500, dtype=dtype, norm=False)
         check(run_attn(gpu_lib, inp), oracle_out(inp), inp.v, dtype, "norm off")
 
@@ -92,6 +92,44 @@ def test_outlier_keys_norm_off_fp32_state(gpu_lib):
     o_ref, parts = oracle.linear_attn(inp.q, inp.k, inp.v, None, None, inp.H, inp.D, inp.eps, return_parts=True)
     assert parts["z"].max() > 65504.0
     check(run_attn(gpu_lib, inp), o_ref, inp.v, "bf16", "outlier K, norm off")
+
+
+def test_outlier_keys_norm_off_f16_io(gpu_lib):
+    """The same keys stored as IEEE binary16 (largest finite value 65504): z exceeds the binary16 range,
+    yet the state stays in fp32 and the output is finite and within the gates."""
+    inp = gen_attn(4, 1, 4096, dtype="f16", k_scale=30.0, outlier_frac=0.01, norm=False)
+    o_ref, parts = oracle.linear_attn(inp.q, inp.k, inp.v, None, None, inp.H, inp.D, inp.eps, return_parts=True)
+    assert parts["z"].max() > 65504.0
+    o = run_attn(gpu_lib, inp)
+    assert o.dtype == torch.float16 and torch.isfinite(o).all()
+    check(o, o_ref, inp.v, "f16", "outlier K, norm off, f16")
+
+
+@pytest.mark.parametrize("kind", ["1", "2"])
+def test_f16_io_output_kernels(gpu_lib, kind):
+    """binary16 I/O with the QK-Norm on, through both output kernels, several tiles and a ragged tail,
+    NaN-poisoned output buffer, two calls bit-identical."""
+    inp = gen_attn(43, 2, 2100, dtype="f16")
+    q, k, v = dev(inp.q, "f16"), dev(inp.k, "f16"), dev(inp.v, "f16")
+    gq, gk = gains_dev(inp.gq), gains_dev(inp.gk)
+
+    def run():
+        out = torch.full(q.shape, float("nan"), device="cuda", dtype=torch.float16)
+        o = gpu_lib.linear_attn(q, k, v, gq, gk, inp.H, inp.D, inp.eps, out=out)
+        torch.cuda.synchronize()
+        return o
+
+    o1 = _with_env("SANA_OUT_KERNEL", kind, run)
+    o2 = _with_env("SANA_OUT_KERNEL", kind, run)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    check(o1, oracle_out(inp), inp.v, "f16", f"f16 out kernel {kind}")
+
+
+def test_f16_head_counts_and_chunked_state(gpu_lib):
+    """Odd and large head counts, and a token count split over several state chunks (the reduce)."""
+    for H, N in ((3, 150), (71, 150), (80, 150), (70, 16384)):
+        inp = gen_attn(3000 + H, 1, N, H=H, dtype="f16")
+        check(run_attn(gpu_lib, inp), oracle_out(inp), inp.v, "f16", f"f16 H={H} N={N}")
 
 
 def test_deterministic_bitwise(gpu_lib):
