@@ -22,6 +22,7 @@ struct AttnPlan {
   int Tc;               // tokens per KV chunk (multiple of 64)
   int NC;               // number of chunks per sample
   int out_kind;         // bf16 output kernel: kOutPersist or kOutTile
+  bool out_strided;     // persistent output kernel: block b takes tiles b, b + G, ... (else a contiguous run)
   int num_cus;          // compute units of the current device
   size_t off_rk, off_rq, off_part, off_S32, off_z, off_Sop;
   size_t ws_bytes;

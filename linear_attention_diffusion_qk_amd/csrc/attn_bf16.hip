@@ -300,16 +300,19 @@ __device__ __forceinline__ u32x4 swap_halves(u32x4 old, u32x4 src) {
 
 // ---------------------------------------------------------------------------------------------
 // Persistent output kernel.  One block per CU keeps S', z' and the query sign masks of the current
-// sample in LDS and walks a contiguous run of 16-token tiles.  Wave w owns head pairs
-// [w*PPW, w*PPW + PPW).  A head pair of one token is one 128-byte span of the Q or O row, so every
-// load and store instruction touches 8 whole rows x 128 bytes: load j of a pair gives lane
-// (n = l%16, kg = l/16) the 16 bytes (token 8j + n%8, head 2p + n/8, dims 8kg..8kg+7), and one DPP
-// swap of the row halves turns the two loads into the MFMA B operands of the two heads
-// (lane (n, kg) = token n, dims 8kg..8kg+7); stores use the inverse swap.  Q tiles alternate
-// between two register sets: each step first issues the loads of the next tile (unconditionally,
-// clamped to the last tile, so the wait for the current tile leaves them in flight) and then
-// consumes the current one; nothing else in the tile loop reads global memory.  The row sums of
-// squares are combined across waves through LDS in a fixed order.
+// sample in LDS and walks a sequence of 16-token tiles: a contiguous run, or tiles b, b + G, b + 2G,
+// ... (G blocks; all blocks then sweep the tensor together, which reads and writes HBM faster when a
+// sample spans many tiles per block).  Wave w owns head pairs [w*PPW, w*PPW + PPW).  A head pair of
+// one token is one 128-byte span of the Q or O row, so every load and store instruction touches 8
+// whole rows x 128 bytes:
+// load j of a pair gives lane (n = l%16, kg = l/16) the 16 bytes (token 8j + n%8, head 2p + n/8,
+// dims 8kg..8kg+7), and one DPP swap of the row halves turns the two loads into the MFMA B operands
+// of the two heads (lane (n, kg) = token n, dims 8kg..8kg+7); stores use the inverse swap.  Q tiles
+// alternate between two register sets: each step first issues the loads of the next tile and then
+// consumes the current one.  Loads and stores are range-checked buffer operations over the tile's
+// rows, so rows past the end and a next tile that does not exist cost no memory traffic while every
+// step still issues the same instructions (the waits for a tile's loads never cover other
+// operations).  The row sums of squares are combined across waves through LDS in a fixed order.
 // ---------------------------------------------------------------------------------------------
 template <int PPW, bool NORM, bool F16>
 __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restrict__ q, int64_t ldq,
@@ -330,27 +333,37 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
   const int tok8 = n16 & 7, hsel = n16 >> 3;  // load/store role of this lane within a head pair
   const int tiles_per_sample = (N + 15) / 16;
   const int64_t total = (int64_t)B * tiles_per_sample;
-  const int64_t tau0 = (int64_t)blockIdx.x * tiles_per_block;
-  const int64_t tau_end = min(total, tau0 + tiles_per_block);
-  if (tau0 >= tau_end) return;
+  const int G = gridDim.x;
+  // Tiles t < lim belong to this block's sequence; t >= lim means "none".
+  // tiles_per_block = 0: tiles b, b + G, b + 2G, ... (all blocks sweep the tensor together).
+  const bool strided = tiles_per_block == 0;
+  const int64_t T0 = strided ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * tiles_per_block;
+  const int64_t lim = strided ? total : min(total, T0 + tiles_per_block);
+  if (T0 >= lim) return;
+  const int64_t T1 = strided ? T0 + G : T0 + 1;
 
-  // Raw loads of one tile: qr[2*i + j] = load j of pair w*PPW + i.  Addresses are clamped into the
-  // tensor; lanes past N or H are never stored.
-  auto load_tile = [&](int64_t tau, u32x4* qr) {
-    tau = min(tau, tau_end - 1);
-    const int64_t bb = tau / tiles_per_sample;
-    const int n0 = (int)(tau - bb * tiles_per_sample) * 16;
+  // Raw loads of one tile: qr[2*i + j] = load j of pair w*PPW + i; all zero, without memory traffic,
+  // for rows past N and for t >= lim.  Head indices are clamped into the row; lanes past N or H are
+  // never stored.
+  auto load_tile = [&](int64_t t, u32x4* qr) {
+    const bool valid = t < lim;
+    const int64_t tt = valid ? t : T0;
+    const int64_t bb = tt / tiles_per_sample;
+    const int n0 = (int)(tt - bb * tiles_per_sample) * 16;
+    const int rows = valid ? min(16, N - n0) : 0;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        make_rsrc(q + (bb * N + n0) * ldq, rows > 0 ? (uint32_t)(((rows - 1) * ldq + (int64_t)H * kHeadDim) * 2) : 0u);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const uint16_t* row = q + (bb * N + min(n0 + 8 * j + tok8, N - 1)) * ldq + kg * 8;
+      const uint32_t roff = (uint32_t)(((8 * j + tok8) * ldq + kg * 8) * 2);
 #pragma unroll
       for (int i = 0; i < PPW; ++i)
-        qr[2 * i + j] = load16(row + min(2 * (w * PPW + i) + hsel, H - 1) * kHeadDim);
+        qr[2 * i + j] = buffer_load16(rsrc, roff + (uint32_t)(min(2 * (w * PPW + i) + hsel, H - 1) * kHeadDim * 2));
     }
   };
 
   int64_t cur_b = -1;
-  auto step = [&](int64_t tau, u32x4* cur, u32x4* nxt) {
+  auto step = [&](int k, int64_t tau, int64_t tau_next, u32x4* cur, u32x4* nxt) {
     const int64_t bb = tau / tiles_per_sample;
     const int n0 = (int)(tau - bb * tiles_per_sample) * 16;
     if (bb != cur_b) {  // uniform across the block
@@ -364,7 +377,7 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
       __syncthreads();
       cur_b = bb;
     }
-    load_tile(tau + 1, nxt);
+    load_tile(tau_next, nxt);
     // MFMA operand layout: lane (n16, kg) = token n16 of the tile, dims 8kg..8kg+7.
     u32x4 bq[2 * PPW];
 #pragma unroll
@@ -382,7 +395,7 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
           for (int u = 0; u < 4; ++u) ss = dot2_h<F16>(bq[i][u], bq[i][u], ss);
         }
       ss = sum_over_lane_groups(ss);
-      float* sb = ssq + (tau & 1) * 8 * 16;
+      float* sb = ssq + (k & 1) * 8 * 16;
       if (kg == 0) sb[w * 16 + n16] = ss;
       __syncthreads();
       float tot = 0.f;
@@ -390,8 +403,7 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
       epsr = eps * sqrtf(tot * inv_C + eps);  // eps / r_q
     }
     // Output rows of this tile as one range-checked buffer: every store instruction is issued (lanes
-    // past N or H get an out-of-range offset), so the store count per step is fixed and the waits for
-    // the next tile's loads never include this tile's stores.
+    // past N or H get an out-of-range offset), so the store count per step is fixed.
     const int rows = min(16, N - n0);
     const __amdgpu_buffer_rsrc_t orsrc =
         make_rsrc(out + (bb * N + n0) * ldo, (uint32_t)(((rows - 1) * ldo + (int64_t)H * kHeadDim) * 2));
@@ -421,13 +433,14 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
       }
     }
   };
+  const int64_t tile_step = strided ? G : 1;
 
   u32x4 qa[2 * PPW], qb[2 * PPW];
   {
     // Each wave copies the first sample's operands of its own heads (the only ones it reads until the
     // sample changes) ahead of its first Q tile, so the wait below covers only them (vmcnt retires in
     // issue order) and needs no block-wide barrier; the tile's loads stay in flight.
-    const int64_t b0 = tau0 / tiles_per_sample;
+    const int64_t b0 = T0 / tiles_per_sample;
     const int hb = min(H, 2 * w * PPW), he = min(H, 2 * (w + 1) * PPW);
     if (he > hb) {
       dma_to_lds(Sop + (b0 * H + hb) * kOpPerHead, Ss + hb * kOpPerHead, (he - hb) * kOpPerHead * 2, 0, 1, lane);
@@ -435,7 +448,7 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
       dma_to_lds(gsg + hb * kSgnPerHead, Gs + hb * kSgnPerHead, (he - hb) * kSgnPerHead * 4, 0, 1, lane);
     }
     __asm__ __volatile__("" ::: "memory");
-    load_tile(tau0, qa);
+    load_tile(T0, qa);
     __asm__ __volatile__("" ::: "memory");
     static_assert(2 * PPW <= 15, "vmcnt immediate holds 4 low bits here");
     __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * PPW));  // vmcnt <= 2*PPW, expcnt/lgkmcnt not waited on
@@ -445,14 +458,17 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
   // The first step is peeled so that the loop is entered, like its back edge, with one tile's loads and
   // one tile's stores outstanding; both loop steps run unconditionally.  With no control-flow merge of
   // different outstanding counts the compiler's waits for a tile's loads never cover earlier stores.
-  int64_t tau = tau0;
-  step(tau, qa, qb);
-  ++tau;
-  for (; tau + 1 < tau_end; tau += 2) {
-    step(tau, qb, qa);
-    step(tau + 1, qa, qb);
+  int64_t t1 = T1;
+  step(0, T0, t1, qa, qb);
+  int k = 1;
+  while (t1 < lim) {
+    const int64_t t2 = t1 + tile_step;
+    step(k, t1, t2, qb, qa);
+    if (t2 >= lim) break;
+    t1 = t2 + tile_step;
+    step(k + 1, t2, t1, qa, qb);
+    k += 2;
   }
-  if (tau < tau_end) step(tau, qb, qa);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -569,7 +585,8 @@ static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t l
     const int64_t tiles = (int64_t)B * ((N + 15) / 16);
     const int blocks = (int)std::min<int64_t>(num_cus, tiles);
     const int per = (int)((tiles + blocks - 1) / blocks);
-    const int nblk = (int)((tiles + per - 1) / per);
+    const int nblk = p.out_strided ? blocks : (int)((tiles + per - 1) / per);
+    const int per_arg = p.out_strided ? 0 : per;  // 0: strided tiles
     const size_t lds = out_persist_lds_bytes(H);
     const int nw = ((H + 1) / 2 + kPersistPPW - 1) / kPersistPPW;
     static bool attr_set = false;  // one flag per storage type
@@ -582,10 +599,10 @@ static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t l
     }
     if (p.norm)
       SANA_LAUNCH("out", out_persist_bf16<kPersistPPW, true, F16><<<nblk, nw * 64, lds, stream>>>(
-                             q, ldq, gsg, Sop, zop, B, N, H, eps, inv_C, out, ldo, per));
+                             q, ldq, gsg, Sop, zop, B, N, H, eps, inv_C, out, ldo, per_arg));
     else
       SANA_LAUNCH("out", out_persist_bf16<kPersistPPW, false, F16><<<nblk, nw * 64, lds, stream>>>(
-                             q, ldq, gsg, Sop, zop, B, N, H, eps, inv_C, out, ldo, per));
+                             q, ldq, gsg, Sop, zop, B, N, H, eps, inv_C, out, ldo, per_arg));
     return hipGetLastError();
   }
   constexpr int HPW = 18;

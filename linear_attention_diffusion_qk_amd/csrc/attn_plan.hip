@@ -57,6 +57,13 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
                 (int64_t)B * ((N + 15) / 16) >= 2 * p.num_cus && env_int("SANA_OUT_KERNEL", kOutPersist) != kOutTile)
                    ? kOutPersist
                    : kOutTile;
+  // Strided tiles once a sample spans at least two tiles per block (so that a block's tiles stay within
+  // few samples); SANA_OUT_SCHED=1 asks for contiguous runs.
+  {
+    const int64_t tiles = (int64_t)B * ((N + 15) / 16);
+    const int64_t blocks = std::min<int64_t>(p.num_cus, tiles);
+    p.out_strided = p.out_kind == kOutPersist && (N + 15) / 16 >= 2 * blocks && env_int("SANA_OUT_SCHED", 2) != 1;
+  }
   const size_t BH = (size_t)B * H;
   size_t off = 0;
   p.off_rk = off;   off = align_up(off + (norm ? (size_t)B * N * 4 : 0), 256);

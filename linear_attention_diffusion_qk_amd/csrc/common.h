@@ -92,6 +92,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
+// A load whose range check fails returns zeros without a memory access.
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
 __device__ __forceinline__ f32x4 loadf4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
 // Sum over the 4 lanes {l, l^16, l^32, l^48} (the four 16-lane groups of a wave64).

@@ -231,6 +231,28 @@ def test_output_kernels_agree_with_oracle(gpu_lib, kind):
     check(o, oracle_out(inp), inp.v, "bf16", f"out kernel {kind}")
 
 
+@pytest.mark.parametrize("B,N,norm", [(1, 12345, True), (2, 8200, True), (1, 9000, False)])
+def test_persistent_schedules_agree(gpu_lib, B, N, norm):
+    """Persistent output kernel with strided tiles (the default at these sizes) and with contiguous
+    runs: every tile written (NaN-poisoned output), both bit-identical, within the gates.  Covers a
+    ragged last tile, a sample change inside the strided sweep and the norm-off variant."""
+    inp = gen_attn(47 + N, B, N, dtype="bf16", norm=norm)
+    q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
+    gq, gk = gains_dev(inp.gq), gains_dev(inp.gk)
+
+    def run():
+        out = torch.full(q.shape, float("nan"), device="cuda", dtype=torch.bfloat16)
+        o = gpu_lib.linear_attn(q, k, v, gq, gk, inp.H, inp.D, inp.eps, out=out)
+        torch.cuda.synchronize()
+        return o
+
+    o_strided = _with_env("SANA_OUT_SCHED", "2", run)
+    o_runs = _with_env("SANA_OUT_SCHED", "1", run)
+    assert not torch.isnan(o_strided).any() and not torch.isnan(o_runs).any()
+    assert torch.equal(o_strided.view(torch.int16), o_runs.view(torch.int16))
+    check(o_strided, oracle_out(inp), inp.v, "bf16", f"schedules B={B} N={N} norm={norm}")
+
+
 @pytest.mark.parametrize("kind", ["1", "2"])
 def test_mixed_scale_query_rows(gpu_lib, kind):
     rows = [(0, 3), (0, 64), (1, 100), (1, 4000)]
