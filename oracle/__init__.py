@@ -21,3 +21,4 @@ from .linear_attn import (  # noqa: F401
     rms_inverse,
     split_heads,
 )
+from .w8a8 import qkv_w8a8_linear_attn, quantize_rows, quantize_weight, w8a8_project  # noqa: F401

@@ -1,0 +1,119 @@
+"""Pins of the W8A8 oracle (no GPU needed).
+
+The projection in 8-bit weights and activations: "Sana: Efficient High-Resolution Image Synthesis
+with Linear Diffusion Transformers" (paper notes), section 7 "on-device deployment".  Pinned by a
+hand-worked quantisation example (tests/golden/w8a8_quant_rows.txt), the rounding error bound of a
+symmetric uniform quantiser, power-of-two scale invariance, exact integer brute force of the
+projection, a closed-form bound against the unquantised fp64 projection, and the transposed weight
+layout on a hand example.
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_rows():
+    xs, qs, ss = [], [], []
+    with open(os.path.join(GOLDEN, "w8a8_quant_rows.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            if key == "x":
+                xs.append([float(v) for v in vals])
+            elif key == "q":
+                qs.append([int(v) for v in vals])
+            elif key == "s":
+                ss.append(np.array(int(vals[0], 16), dtype=np.uint32).view(np.float32))
+    return np.array(xs, np.float32), np.array(qs, np.int8), np.array(ss, np.float32)
+
+
+def test_golden_quant_rows_bit_exact():
+    x, q_ref, s_ref = _golden_rows()
+    q, s = oracle.quantize_rows(x)
+    assert np.array_equal(q, q_ref)
+    assert np.array_equal(s.view(np.uint32), s_ref.view(np.uint32))
+
+
+def _bf16_rows(rng, rows, C, scale=1.0):
+    x = (scale * rng.standard_normal((rows, C))).astype(np.float32)
+    b = x.view(np.uint32)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000).astype(np.uint32).view(np.float32)
+
+
+def test_quant_error_bound_and_extremes():
+    """|x - q s| <= s/2 (up to the fp32 rounding of 127/amax), the largest |x| maps to +-127."""
+    rng = np.random.default_rng(1)
+    x = _bf16_rows(rng, 64, 2240, scale=3.0)
+    x[5, 17] = 0.0
+    q, s = oracle.quantize_rows(x)
+    err = np.abs(x.astype(np.float64) - q.astype(np.float64) * s[:, None].astype(np.float64))
+    assert np.all(err <= 0.5 * s[:, None] * (1 + 1e-5) + 1e-30)
+    amax_idx = np.argmax(np.abs(x), axis=1)
+    assert np.all(np.abs(q[np.arange(64), amax_idx].astype(int)) == 127)
+    assert np.all(np.abs(q.astype(int)) <= 127)
+    assert q[5, 17] == 0
+
+
+def test_quant_power_of_two_invariance_and_row_independence():
+    """Scaling a row by 2^k scales its s by 2^k and keeps its codes; other rows are untouched."""
+    rng = np.random.default_rng(2)
+    x = _bf16_rows(rng, 8, 448)
+    q0, s0 = oracle.quantize_rows(x)
+    y = x.copy()
+    y[3] *= np.float32(2.0 ** 7)
+    q1, s1 = oracle.quantize_rows(y)
+    assert np.array_equal(q0, q1)
+    assert s1[3] == s0[3] * np.float32(2.0 ** 7)
+    assert np.array_equal(np.delete(s0, 3), np.delete(s1, 3))
+
+
+def test_projection_exact_against_integer_brute_force():
+    """w8a8_project = (sum_c xq*wq) * sx * sw with the integer sum exact (Python ints, Fractions)."""
+    rng = np.random.default_rng(3)
+    M, C, NO = 3, 64, 12
+    xq = rng.integers(-127, 128, size=(M, C)).astype(np.int8)
+    wq = rng.integers(-127, 128, size=(NO, C)).astype(np.int8)
+    sx = rng.uniform(0.01, 0.1, size=M).astype(np.float32)
+    sw = rng.uniform(0.001, 0.01, size=NO).astype(np.float32)
+    got = oracle.w8a8_project(xq, sx, wq, sw)
+    for m in range(M):
+        for n in range(NO):
+            acc = sum(int(xq[m, c]) * int(wq[n, c]) for c in range(C))
+            exact = Fraction(acc) * Fraction(float(sx[m])) * Fraction(float(sw[n]))
+            assert abs(Fraction(got[m, n]) - exact) <= abs(exact) * Fraction(1, 2 ** 50)
+
+
+def test_weight_quant_is_per_output_column_and_transposed():
+    """W [C=2, 3] by hand: column n has amax a_n; row n of Wt_q holds that column's codes."""
+    w = np.array([[1.0, -2.0, 0.5],
+                  [-0.5, 1.0, 0.25]], np.float32)
+    wt_q, sw = oracle.quantize_weight(w)
+    assert wt_q.shape == (3, 2)
+    assert np.array_equal(wt_q, np.array([[127, -64], [-127, 64], [127, 64]], np.int8))
+    assert np.array_equal(sw, np.array([1.0, 2.0, 0.5], np.float32) / np.float32(127))
+
+
+def test_w8a8_qkv_within_quantisation_bound_of_fp64_projection():
+    """|xW - W8A8(x, W)| <= sum_c |x_c| dW + |W_c| dx + dx dW with dx = s_x/2, dW = s_w/2 per element."""
+    rng = np.random.default_rng(4)
+    M, C = 16, 320
+    x = _bf16_rows(rng, M, C)
+    w = (0.02 * rng.standard_normal((C, 3 * C))).astype(np.float32)
+    wt_q, sw = oracle.quantize_weight(w)
+    xq, sx = oracle.quantize_rows(x)
+    got = oracle.w8a8_project(xq, sx, wt_q, sw)
+    ref = x.astype(np.float64) @ w.astype(np.float64)
+    dx = 0.5 * sx.astype(np.float64)[:, None] * (1 + 1e-5)
+    dw = 0.5 * sw.astype(np.float64)[None, :] * (1 + 1e-5)
+    bound = (np.abs(x).astype(np.float64).sum(1, keepdims=True) * dw
+             + dx * np.abs(w).astype(np.float64).sum(0, keepdims=True) + C * dx * dw)
+    err = np.abs(got - ref)
+    assert np.all(err <= bound)
+    assert err.max() > 0  # the quantisation is not a no-op
