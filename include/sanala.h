@@ -32,6 +32,7 @@
 #define SANALA_H
 
 #include <hip/hip_runtime_api.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -91,6 +92,43 @@ sana_status_t sana_qkv_linear_attn_fwd(const void* x, const void* Wqkv,
                                        const float* gq, const float* gk,
                                        int B, int N, int H, int D, float eps,
                                        void* out, hipStream_t stream);
+
+/*
+ * sana_qkv_w8a8_linear_attn_fwd -- the fused front end with the projection in W8A8 (the Sana notes,
+ * section 7: 8-bit weights and activations for deployment, with the linear attention kept in full
+ * precision).  x is quantised per token on the device (sana_quantize_rows_i8), the projection runs on
+ * int8 MFMA with exact int32 sums, qkv = bf16((sum_c xq[m,c] * Wt_q[n,c]) * x_scale[m] * w_scale[n])
+ * (fp32 products in that order), and the attention is that of sana_linear_attn_fwd on bf16 q | k | v.
+ *
+ *   x        device bf16 [B, N, C], C = H*D, contiguous, 16-byte aligned.
+ *   Wt_q     device int8 [3C, C] row-major: the quantised weight transposed, row n holding the C input
+ *            weights of output column n (q = rows [0,C), k = [C,2C), v = [2C,3C)); 16-byte aligned.
+ *   w_scale  device fp32 [3C]: dequantisation scale of each output column (W[:, n] ~ w_scale[n] *
+ *            Wt_q[n, :]); 16-byte aligned.  The scale granularity is a reading: the pages do not fix it.
+ *   gq, gk, B, N, H, D, eps, out, stream as for sana_qkv_linear_attn_fwd; C must be a multiple of 64
+ *            (else SANA_ERR_UNSUPPORTED).
+ *
+ * Scratch (stream-ordered): int8 x, its row scales and the bf16 qkv.  Errors as above.
+ */
+sana_status_t sana_qkv_w8a8_linear_attn_fwd(const void* x, const void* Wt_q, const float* w_scale,
+                                            const float* gq, const float* gk,
+                                            int B, int N, int H, int D, float eps,
+                                            void* out, hipStream_t stream);
+
+/*
+ * sana_quantize_rows_i8 -- per-row symmetric int8 quantisation of bf16 x [rows, C] (the activation
+ * half of W8A8): with a = max_c |x[r, c]|, xq = clamp(rne(x * (127 / a)), -127, 127) and
+ * x_scale[r] = a / 127, each step in fp32 with correctly rounded division; a row of zeros gives
+ * xq = 0 and x_scale = 0.  NaN inputs are not checked.
+ *
+ *   x        device bf16 [rows, C], contiguous, 16-byte aligned; C a multiple of 8, rows <= 2^32.
+ *   xq       device int8 [rows, C], 16-byte aligned, not overlapping x; fully overwritten.
+ *   x_scale  device fp32 [rows]; fully overwritten.
+ *
+ * Returns SANA_OK once enqueued on `stream`; argument errors as above.
+ */
+sana_status_t sana_quantize_rows_i8(const void* x, int64_t rows, int C, void* xq, float* x_scale,
+                                    hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* sana_status_string(sana_status_t status);

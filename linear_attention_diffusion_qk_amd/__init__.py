@@ -7,8 +7,12 @@ from ._lib import EXPORTS, SanaError, library_path, load_library, status_string 
 from .api import (  # noqa: F401
     linear_attn,
     qkv_linear_attn,
+    qkv_w8a8_linear_attn,
+    quantize_rows_i8,
     sana_linear_attn_fwd,
     sana_qkv_linear_attn_fwd,
+    sana_qkv_w8a8_linear_attn_fwd,
+    sana_quantize_rows_i8,
     sana_timing_enable,
     sana_timing_last,
 )

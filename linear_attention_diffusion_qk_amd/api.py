@@ -58,6 +58,24 @@ def sana_qkv_linear_attn_fwd(x, Wqkv, gq, gk, B: int, N: int, H: int, D: int, ep
         raise SanaError(st, "sana_qkv_linear_attn_fwd")
 
 
+def sana_qkv_w8a8_linear_attn_fwd(x, Wt_q, w_scale, gq, gk, B: int, N: int, H: int, D: int, eps: float, out,
+                                  stream=None) -> None:
+    _check_dev(x, Wt_q, w_scale, gq, gk, out)
+    lib = _lib.load_library()
+    st = lib.sana_qkv_w8a8_linear_attn_fwd(_ptr(x), _ptr(Wt_q), _ptr(w_scale), _ptr(gq), _ptr(gk), int(B), int(N),
+                                           int(H), int(D), float(eps), _ptr(out), _stream_handle(stream))
+    if st != _lib.SANA_OK:
+        raise SanaError(st, "sana_qkv_w8a8_linear_attn_fwd")
+
+
+def sana_quantize_rows_i8(x, rows: int, C: int, xq, x_scale, stream=None) -> None:
+    _check_dev(x, xq, x_scale)
+    lib = _lib.load_library()
+    st = lib.sana_quantize_rows_i8(_ptr(x), int(rows), int(C), _ptr(xq), _ptr(x_scale), _stream_handle(stream))
+    if st != _lib.SANA_OK:
+        raise SanaError(st, "sana_quantize_rows_i8")
+
+
 def linear_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gq: Optional[torch.Tensor],
                 gk: Optional[torch.Tensor], H: int, D: int = 32, eps: float = 1e-6,
                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -90,6 +108,34 @@ def qkv_linear_attn(x: torch.Tensor, Wqkv: torch.Tensor, gq: Optional[torch.Tens
         out = torch.empty_like(x)
     sana_qkv_linear_attn_fwd(x, Wqkv, gq, gk, B, N, H, D, eps, out)
     return out
+
+
+def qkv_w8a8_linear_attn(x: torch.Tensor, Wt_q: torch.Tensor, w_scale: torch.Tensor, gq: Optional[torch.Tensor],
+                         gk: Optional[torch.Tensor], H: int, D: int = 32, eps: float = 1e-6,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x [B, N, C] bf16, Wt_q [3C, C] int8 (W transposed, quantised per output column), w_scale [3C] fp32
+    -> linear attention of the W8A8 projection's q | k | v blocks (x quantised per token inside)."""
+    if x.dim() != 3 or x.dtype != torch.bfloat16 or Wt_q.dtype != torch.int8 or w_scale.dtype != torch.float32:
+        raise ValueError("x must be bf16 [B, N, C], Wt_q int8 [3C, C] and w_scale float32 [3C]")
+    B, N, C = x.shape
+    if C != H * D or tuple(Wt_q.shape) != (3 * C, C) or w_scale.numel() != 3 * C:
+        raise ValueError("shape mismatch between x, Wt_q, w_scale and H*D")
+    if out is None:
+        out = torch.empty_like(x)
+    sana_qkv_w8a8_linear_attn_fwd(x, Wt_q, w_scale, gq, gk, B, N, H, D, eps, out)
+    return out
+
+
+def quantize_rows_i8(x: torch.Tensor):
+    """bf16 [..., C] -> (int8 codes of the same shape, fp32 per-row scales [...]): the device quantiser."""
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16")
+    C = x.shape[-1]
+    rows = x.numel() // C
+    xq = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    sx = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    sana_quantize_rows_i8(x, rows, C, xq, sx)
+    return xq, sx
 
 
 def sana_timing_enable(enable: bool) -> None:

@@ -56,6 +56,13 @@ int max_heads();
 hipError_t launch_qkv_gemm(const uint16_t* x, const uint16_t* w, uint16_t* qkv, int64_t M, int C, hipStream_t stream,
                            float* k_ssq = nullptr);
 int qkv_gemm_k_parts(int C);
+// W8A8 form: xq int8 [M, C] with per-row scales s_x [M]; wt int8 [3C, C] (W transposed: K contiguous
+// per output column) with per-column scales s_w [3C]; qkv = bf16((sum_c xq*wt) * s_x[m] * s_w[n]).
+// C must be a multiple of 64.  k_ssq as for launch_qkv_gemm.
+hipError_t launch_qkv_gemm_i8(const int8_t* xq, const int8_t* wt, const float* s_x, const float* s_w, uint16_t* qkv,
+                              int64_t M, int C, hipStream_t stream, float* k_ssq = nullptr);
+// Per-row symmetric int8 quantisation of bf16 x [M, C] (C a multiple of 8).
+hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int C, int8_t* xq, float* s_x, hipStream_t stream);
 
 // Measurement hooks (no-ops unless timing is enabled on the calling host thread): an event pair is
 // recorded on `s` around each kernel launch.

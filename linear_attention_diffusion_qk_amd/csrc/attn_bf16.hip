@@ -438,21 +438,41 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
   u32x4 qa[2 * PPW], qb[2 * PPW];
   {
     // Each wave copies the first sample's operands of its own heads (the only ones it reads until the
-    // sample changes) ahead of its first Q tile, so the wait below covers only them (vmcnt retires in
-    // issue order) and needs no block-wide barrier; the tile's loads stay in flight.
+    // sample changes) ahead of its first Q tile, so its waits cover only them (vmcnt retires in issue
+    // order) and need no block-wide barrier; the tile's loads stay in flight.  (Staging through
+    // registers measured 0.9 us per call faster here than direct global->LDS loads.)
     const int64_t b0 = T0 / tiles_per_sample;
     const int hb = min(H, 2 * w * PPW), he = min(H, 2 * (w + 1) * PPW);
-    if (he > hb) {
-      dma_to_lds(Sop + (b0 * H + hb) * kOpPerHead, Ss + hb * kOpPerHead, (he - hb) * kOpPerHead * 2, 0, 1, lane);
-      dma_to_lds(zop + (b0 * H + hb) * kZopPerHead, Zs + hb * kZopPerHead, (he - hb) * kZopPerHead * 2, 0, 1, lane);
-      dma_to_lds(gsg + hb * kSgnPerHead, Gs + hb * kSgnPerHead, (he - hb) * kSgnPerHead * 4, 0, 1, lane);
-    }
+    // Range-checked buffer loads (lanes past the region read zeros, no traffic), the first tile's loads
+    // behind them, then LDS stores of the region only.
+    const int nh = max(0, he - hb);
+    const __amdgpu_buffer_rsrc_t rS = make_rsrc(Sop + (b0 * H + hb) * kOpPerHead, (uint32_t)(nh * kOpPerHead * 2));
+    const __amdgpu_buffer_rsrc_t rZ = make_rsrc(zop + (b0 * H + hb) * kZopPerHead, (uint32_t)(nh * kZopPerHead * 2));
+    const __amdgpu_buffer_rsrc_t rG = make_rsrc(gsg + hb * kSgnPerHead, (uint32_t)(nh * kSgnPerHead * 4));
+    constexpr int CS = 2 * PPW * kOpPerHead * 2 / 1024, CZ = (2 * PPW * kZopPerHead * 2 + 1023) / 1024,
+                  CG = (2 * PPW * kSgnPerHead * 4 + 1023) / 1024;
+    u32x4 st[CS + CZ + CG];
+#pragma unroll
+    for (int c = 0; c < CS; ++c) st[c] = buffer_load16(rS, c * 1024 + lane * 16);
+#pragma unroll
+    for (int c = 0; c < CZ; ++c) st[CS + c] = buffer_load16(rZ, c * 1024 + lane * 16);
+#pragma unroll
+    for (int c = 0; c < CG; ++c) st[CS + CZ + c] = buffer_load16(rG, c * 1024 + lane * 16);
     __asm__ __volatile__("" ::: "memory");
     load_tile(T0, qa);
     __asm__ __volatile__("" ::: "memory");
-    static_assert(2 * PPW <= 15, "vmcnt immediate holds 4 low bits here");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * PPW));  // vmcnt <= 2*PPW, expcnt/lgkmcnt not waited on
-    __asm__ __volatile__("" ::: "memory");
+    char* dS = reinterpret_cast<char*>(Ss + hb * kOpPerHead);
+    char* dZ = reinterpret_cast<char*>(Zs + hb * kZopPerHead);
+    char* dG = reinterpret_cast<char*>(Gs + hb * kSgnPerHead);
+#pragma unroll
+    for (int c = 0; c < CS; ++c)
+      if (c * 1024 + lane * 16 < nh * kOpPerHead * 2) store16(dS + c * 1024 + lane * 16, st[c]);
+#pragma unroll
+    for (int c = 0; c < CZ; ++c)
+      if (c * 1024 + lane * 16 < nh * kZopPerHead * 2) store16(dZ + c * 1024 + lane * 16, st[CS + c]);
+#pragma unroll
+    for (int c = 0; c < CG; ++c)
+      if (c * 1024 + lane * 16 < nh * kSgnPerHead * 4) store16(dG + c * 1024 + lane * 16, st[CS + CZ + c]);
     cur_b = b0;
   }
   // The first step is peeled so that the loop is entered, like its back edge, with one tile's loads and

@@ -1,7 +1,9 @@
-// QKV projection qkv[M, 3C] = x[M, C] @ W[C, 3C] on gfx950 MFMA (bf16 in, fp32 accumulate, bf16 out).
+// QKV projection qkv[M, 3C] = x[M, C] @ W[C, 3C] on gfx950 MFMA (bf16 in, fp32 accumulate, bf16 out),
+// and its W8A8 form (int8 x and W with per-row and per-column fp32 scales, int32 accumulate, bf16 out).
 //
 // The projection that the Sana notes (section 7, on-device deployment) fuse with ReLU(K)^T V; here it
-// is a separate dense contraction ahead of the attention kernels.
+// is a separate dense contraction ahead of the attention kernels.  The same notes deploy the model with
+// 8-bit weights and activations while keeping the linear attention in full precision.
 //
 // Block tile 256 (rows of x) x 192 (columns of W), K step 32, 4 waves as 2 x 2, wave tile 128 x 96.
 // Tiles of x and W go from global memory straight to LDS (global_load_lds_dwordx4) through a ring of
@@ -17,6 +19,11 @@
 // consecutive output columns of one row per accumulator quad and writes them as one 8-byte store.
 // With at least 8 row panels, block ids congruent mod 8 (one XCD) cover a slab of row panels, and the
 // 32 CUs of an XCD work on 8 row panels x 4 column panels at a time, so their slices stay in its L2.
+//
+// W8A8 (I8): the K step is 64 int8 (the same 64 bytes per x row), W is given transposed, Wt[3C, C]
+// (K contiguous per output column), and its tile [192][64 bytes] is staged and read exactly like the x
+// tile; v_mfma_i32_32x32x32_i8 takes 16 consecutive k per lane from both operands.  The epilogue
+// converts the exact int32 sums to fp32 and scales them by s_x[m] then s_w[n].
 #include "common.h"
 
 #include <algorithm>
@@ -25,10 +32,10 @@
 namespace sanala {
 
 namespace {
-constexpr int BM = 256, BN = 192, BK = 32, STAGES = 4;
+constexpr int BM = 256, BN = 192, BK = 32, STAGES = 4;  // BK in bf16 elements (64 int8 with I8)
 constexpr int kThreads = 256;
 constexpr int A_ROW = BK * 2;                   // 64 bytes per x tile row
-constexpr int B_ROW = BN * 2;                   // 384 bytes per W tile row
+constexpr int B_ROW = BN * 2;                   // 384 bytes per W tile row (bf16); I8: 192 rows of 64 bytes
 constexpr int A_BYTES = BM * A_ROW;             // 16 KB
 constexpr int B_BYTES = BK * B_ROW;             // 12 KB
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;  // 28 KB
@@ -37,6 +44,8 @@ constexpr int B_DMA = B_BYTES / 1024 / 4;       // 3
 constexpr int DMA_PER_STAGE = A_DMA + B_DMA;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
 
 // s_waitcnt with only vmcnt <= n (n < 64); expcnt and lgkmcnt are not waited on.
@@ -71,6 +80,7 @@ struct Roles {
   int xhalf;   // 16-byte k unit 2s + xhalf
   int wn_col;  // W column of nt = 0 read by this lane's transposing read (+ 32 nt)
   int wk;      // W row of sub-step 0, low half (+ 16 s, + 4 for the high half)
+  int wrow;    // I8: Wt row (output column) of nt = 0 (+ 32 nt)
 };
 
 // Operands of one K step (two 16-wide sub-steps) of one wave.
@@ -82,6 +92,7 @@ struct Ops {
 // Reads a K step's operands from a stage buffer.  The roles are taken by value: read through a
 // reference they would be memory accesses of their own, and the compiler could then no longer keep the
 // stage reads apart from the loads still landing in the other buffers.
+template <bool I8>
 __device__ __forceinline__ void read_ops(const char* __restrict__ As, Roles ro, Ops& op) {
   const char* __restrict__ Bs = As + A_BYTES;
 #pragma unroll
@@ -89,6 +100,12 @@ __device__ __forceinline__ void read_ops(const char* __restrict__ As, Roles ro, 
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
       op.xa[s][mt] = as_bf16x8(*reinterpret_cast<const u32x4*>(As + x_addr(ro.xrow + 32 * mt, 2 * s + ro.xhalf)));
+    if (I8) {
+#pragma unroll
+      for (int nt = 0; nt < 3; ++nt)
+        op.wb[s][nt] = as_bf16x8(*reinterpret_cast<const u32x4*>(Bs + x_addr(ro.wrow + 32 * nt, 2 * s + ro.xhalf)));
+      continue;
+    }
 #pragma unroll
     for (int nt = 0; nt < 3; ++nt) {
       const int n = ro.wn_col + 32 * nt;
@@ -101,20 +118,33 @@ __device__ __forceinline__ void read_ops(const char* __restrict__ As, Roles ro, 
   }
 }
 
-__device__ __forceinline__ void mma(const Ops& op, int s, f32x16 (&acc)[3][4]) {
+template <typename Acc>
+__device__ __forceinline__ void mma(const Ops& op, int s, Acc (&acc)[3][4]) {
 #pragma unroll
   for (int nt = 0; nt < 3; ++nt)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op.wb[s][nt], op.xa[s][mt], acc[nt][mt], 0, 0, 0);
+    for (int mt = 0; mt < 4; ++mt) {
+      if constexpr (std::is_same_v<Acc, i32x16>)
+        acc[nt][mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, op.wb[s][nt]),
+                                                            __builtin_bit_cast(i32x4, op.xa[s][mt]), acc[nt][mt], 0, 0, 0);
+      else
+        acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op.wb[s][nt], op.xa[s][mt], acc[nt][mt], 0, 0, 0);
+    }
 }
 }  // namespace
 
-__global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const uint16_t* __restrict__ x,
-                                                            const uint16_t* __restrict__ w,
+// x: bf16 [M, K] (I8: int8 [M, K]); w: bf16 [K, NO] (I8: int8 Wt [NO, K]); s_x [M] and s_w [NO]: I8 only.
+template <bool I8>
+__global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const void* __restrict__ x, const void* __restrict__ w,
+                                                            const float* __restrict__ s_x,
+                                                            const float* __restrict__ s_w,
                                                             uint16_t* __restrict__ y, int M, int K, int NO,
                                                             int mblocks, int nblocks, int slab,
                                                             float* __restrict__ k_ssq, int k_parts) {
+  using Acc = std::conditional_t<I8, i32x16, f32x16>;
+  constexpr int kElem = I8 ? 1 : 2;  // bytes per x / W element
+  const char* const xb = static_cast<const char*>(x);
+  const char* const wbp = static_cast<const char*>(w);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
 
@@ -132,46 +162,54 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const uint16_t* __re
 
   // Per-lane sources of this wave's DMA instructions (the K step is added per stage).  A instruction
   // i covers rows 16i..16i+15 of the x image, B instruction i bytes [1024i, 1024i + 1024) of the W
-  // image.  Rows past M and columns past NO read clamped addresses; their products are never stored.
-  const uint16_t* a_src[A_DMA];
-  const uint16_t* b_src[B_DMA];
+  // image (I8: rows 16i..16i+15 of the Wt image, placed like x).  Rows past M and columns past NO read
+  // clamped addresses; their products are never stored.
+  const char* a_src[A_DMA];
+  const char* b_src[B_DMA];
 #pragma unroll
   for (int a = 0; a < A_DMA; ++a) {
     const int r = 16 * (wave * A_DMA + a) + (lane >> 2);
     const int kc = (lane & 3) ^ xswz(r);
-    a_src[a] = x + (int64_t)min(m0 + r, M - 1) * K + 8 * kc;
+    a_src[a] = xb + (int64_t)min(m0 + r, M - 1) * K * kElem + 16 * kc;
   }
 #pragma unroll
   for (int b = 0; b < B_DMA; ++b) {
-    const int off = 1024 * (wave * B_DMA + b) + 16 * lane;
-    const int k = off / B_ROW, c = (off % B_ROW) / 16;
-    const int nc = c ^ (2 * (k & 3));
-    b_src[b] = w + (int64_t)k * NO + min(n0 + 8 * nc, NO - 8);
+    if (I8) {
+      const int r = 16 * (wave * B_DMA + b) + (lane >> 2);
+      const int kc = (lane & 3) ^ xswz(r);
+      b_src[b] = wbp + (int64_t)min(n0 + r, NO - 1) * K + 16 * kc;
+    } else {
+      const int off = 1024 * (wave * B_DMA + b) + 16 * lane;
+      const int k = off / B_ROW, c = (off % B_ROW) / 16;
+      const int nc = c ^ (2 * (k & 3));
+      b_src[b] = wbp + ((int64_t)k * NO + min(n0 + 8 * nc, NO - 8)) * 2;
+    }
   }
-  const int KT = K / BK;
+  const int KT = K * kElem / A_ROW;
   // Every step issues the same 7 instructions per wave (past the last K step they re-read it into a
   // buffer that is not read again), so the number of outstanding loads is the same at every wait.
   auto issue = [&](char* base, int t) {
-    const int k0 = min(t, KT - 1) * BK;
+    const int tt = min(t, KT - 1);
 #pragma unroll
     for (int a = 0; a < A_DMA; ++a)
-      __builtin_amdgcn_global_load_lds(a_src[a] + k0, (lds_ptr_t)(base + 1024 * (wave * A_DMA + a)), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a_src[a] + tt * A_ROW, (lds_ptr_t)(base + 1024 * (wave * A_DMA + a)), 16, 0,
+                                       0);
 #pragma unroll
     for (int b = 0; b < B_DMA; ++b)
-      __builtin_amdgcn_global_load_lds(b_src[b] + (int64_t)k0 * NO,
+      __builtin_amdgcn_global_load_lds(b_src[b] + (I8 ? (int64_t)tt * A_ROW : (int64_t)tt * BK * NO * 2),
                                        (lds_ptr_t)(base + A_BYTES + 1024 * (wave * B_DMA + b)), 16, 0, 0);
   };
 
-  f32x16 acc[3][4];
+  Acc acc[3][4];
 #pragma unroll
   for (int i = 0; i < 3; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
   const Roles ro{128 * wm + (lane & 31), lane >> 5, 96 * wn + 16 * ((lane >> 4) & 1) + 4 * (lane & 3),
-                 8 * (lane >> 5) + ((lane >> 2) & 3)};
+                 8 * (lane >> 5) + ((lane >> 2) & 3), 96 * wn + (lane & 31)};
 
   // Step t (t % STAGES == S) multiplies operands read during step t - 1.  Between its two sub-steps it
   // waits until stage t + 1 has landed in every wave (stage t + 2 may still be in flight), refills the
@@ -184,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const uint16_t* __re
     wait_vm<DMA_PER_STAGE>();
     __builtin_amdgcn_s_barrier();
     issue(stage_buf<(S + STAGES - 1) % STAGES>(), t + STAGES - 1);
-    read_ops(stage_buf<(S + 1) % STAGES>(), ro, nxt);
+    read_ops<I8>(stage_buf<(S + 1) % STAGES>(), ro, nxt);
     __builtin_amdgcn_sched_barrier(0);
     mma(cur, 1, acc);
   };
@@ -199,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const uint16_t* __re
   issue(stage_buf<2>(), 2);
   wait_vm<2 * DMA_PER_STAGE>();
   __builtin_amdgcn_s_barrier();
-  read_ops(stage_buf<0>(), ro, ops0);
+  read_ops<I8>(stage_buf<0>(), ro, ops0);
   int t = 0;
   for (; t + 3 < KT; t += STAGES) {
     step(S0, t, ops0, ops1);
@@ -213,7 +251,8 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const uint16_t* __re
   wait_vm<0>();  // no load into LDS outlives the block
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the last (unused) operand reads have returned
 
-  // Stores, and (k_ssq) per-row sums of squares of the stored bf16 values that fall in the K block
+  // Stores (I8: after the scaling by s_x[m] and s_w[n]), and (k_ssq) per-row sums of squares of the
+  // stored bf16 values that fall in the K block
   // [K, 2K) (K = C here).  A 32-column tile lies wholly inside or outside that block (C is a multiple of
   // 32), and v_dot2_f32_bf16 squares the packed pairs being stored; the lane sum (tiles, then
   // quads in order) is combined with the other column half of the wave (lanes l, l + 32) and then with
@@ -226,6 +265,7 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const uint16_t* __re
   for (int mt = 0; mt < 4; ++mt) {
     const int m = m0 + 128 * wm + 32 * mt + (lane & 31);
     if (m >= M) continue;
+    const float sxm = I8 ? s_x[m] : 1.f;
 #pragma unroll
     for (int nt = 0; nt < 3; ++nt) {
       const int ntile = n0 + 96 * wn + 32 * nt;
@@ -233,9 +273,17 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const uint16_t* __re
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = ntile + 8 * q + 4 * (lane >> 5);
-        const f32x16& a = acc[nt][mt];
-        const uint32_t p0 = cvt_pk_bf16(a[4 * q], a[4 * q + 1]);
-        const uint32_t p1 = cvt_pk_bf16(a[4 * q + 2], a[4 * q + 3]);
+        float v4[4];
+        if constexpr (I8) {
+          const f32x4 sw = n < NO ? loadf4(s_w + n) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v4[i] = ((float)acc[nt][mt][4 * q + i] * sxm) * sw[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v4[i] = acc[nt][mt][4 * q + i];
+        }
+        const uint32_t p0 = cvt_pk_bf16(v4[0], v4[1]);
+        const uint32_t p1 = cvt_pk_bf16(v4[2], v4[3]);
         if (n < NO) {
           uint32_t* dst = reinterpret_cast<uint32_t*>(y + (int64_t)m * NO + n);
           dst[0] = p0;
@@ -261,6 +309,46 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const uint16_t* __re
 
 int qkv_gemm_k_parts(int C) { return (2 * C - 1) / BN - C / BN + 1; }
 
+// Per-row symmetric int8 quantisation of bf16 x [M, C] (the dynamic activation half of W8A8): with
+// a = max_c |x[m, c]|, q = clamp(rne(x * (127 / a)), -127, 127) and s_x[m] = a / 127, every step in
+// fp32 with correctly rounded division (a = 0 gives q = 0 and s_x = 0).  One wave per row, 16-byte
+// loads; the second pass over the row re-reads it from cache.
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t M, int C,
+                                                         int8_t* __restrict__ xq, float* __restrict__ s_x) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const uint16_t* xr = x + row * C;
+  const int units = C / 8;  // 16-byte units of the row
+  float amax = 0.f;
+  for (int u = lane; u < units; u += 64) {
+    const u32x4 w = load16(xr + 8 * u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  const float inv = amax > 0.f ? 127.f / amax : 0.f;
+  for (int u = lane; u < units; u += 64) {
+    const u32x4 w = load16(xr + 8 * u);
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float v = (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
+      const float qf = fminf(fmaxf(rintf(v * inv), -127.f), 127.f);
+      packed[i >> 2] |= ((uint32_t)(int)qf & 0xffu) << (8 * (i & 3));
+    }
+    *reinterpret_cast<uint2*>(xq + row * C + 8 * u) = make_uint2(packed[0], packed[1]);
+  }
+  if (lane == 0) s_x[row] = amax / 127.f;
+}
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int C, int8_t* xq, float* s_x, hipStream_t stream) {
+  if (C % 8 != 0) return hipErrorInvalidValue;
+  SANA_LAUNCH("quant_rows", quant_rows_kernel<<<(unsigned)((M + 3) / 4), 256, 0, stream>>>(x, M, C, xq, s_x));
+  return hipGetLastError();
+}
+
 hipError_t launch_qkv_gemm(const uint16_t* x, const uint16_t* w, uint16_t* qkv, int64_t M, int C, hipStream_t stream,
                            float* k_ssq) {
   const int NO = 3 * C;
@@ -268,8 +356,22 @@ hipError_t launch_qkv_gemm(const uint16_t* x, const uint16_t* w, uint16_t* qkv, 
   const int mblocks = (int)((M + BM - 1) / BM), nblocks = (NO + BN - 1) / BN;
   const int slab = mblocks >= 8 ? (mblocks + 7) / 8 : 0;
   const int64_t blocks = slab > 0 ? (int64_t)8 * slab * nblocks : (int64_t)mblocks * nblocks;
-  SANA_LAUNCH("qkv_gemm", qkv_gemm_kernel<<<(unsigned)blocks, kThreads, 0, stream>>>(
-                              x, w, qkv, (int)M, C, NO, mblocks, nblocks, slab, k_ssq, qkv_gemm_k_parts(C)));
+  SANA_LAUNCH("qkv_gemm", qkv_gemm_kernel<false><<<(unsigned)blocks, kThreads, 0, stream>>>(
+                              x, w, nullptr, nullptr, qkv, (int)M, C, NO, mblocks, nblocks, slab, k_ssq,
+                              qkv_gemm_k_parts(C)));
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_gemm_i8(const int8_t* xq, const int8_t* wt, const float* s_x, const float* s_w, uint16_t* qkv,
+                              int64_t M, int C, hipStream_t stream, float* k_ssq) {
+  const int NO = 3 * C;
+  if (C % (2 * BK) != 0 || M > (1LL << 30)) return hipErrorInvalidValue;
+  const int mblocks = (int)((M + BM - 1) / BM), nblocks = (NO + BN - 1) / BN;
+  const int slab = mblocks >= 8 ? (mblocks + 7) / 8 : 0;
+  const int64_t blocks = slab > 0 ? (int64_t)8 * slab * nblocks : (int64_t)mblocks * nblocks;
+  SANA_LAUNCH("qkv_gemm_i8", qkv_gemm_kernel<true><<<(unsigned)blocks, kThreads, 0, stream>>>(
+                                 xq, wt, s_x, s_w, qkv, (int)M, C, NO, mblocks, nblocks, slab, k_ssq,
+                                 qkv_gemm_k_parts(C)));
   return hipGetLastError();
 }
 

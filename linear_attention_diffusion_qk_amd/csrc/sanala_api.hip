@@ -181,3 +181,64 @@ extern "C" sana_status_t sana_qkv_linear_attn_fwd(const void* x, const void* Wqk
   const hipError_t ef = hipFreeAsync(ws, stream);
   return (e == hipSuccess && ef == hipSuccess) ? SANA_OK : SANA_ERR_HIP;
 }
+
+
+extern "C" sana_status_t sana_quantize_rows_i8(const void* x, int64_t rows, int C, void* xq, float* x_scale,
+                                               hipStream_t stream) {
+  if (!x || !xq || !x_scale || rows < 1 || C < 1) return SANA_ERR_INVALID_ARG;
+  if (C % 8 != 0 || rows > (int64_t(1) << 32)) return SANA_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(xq)) return SANA_ERR_MISALIGNED;
+  if (overlaps(xq, (size_t)rows * C, x, (size_t)rows * C * 2)) return SANA_ERR_INVALID_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SANA_ERR_HIP;
+  g_timing.count = 0;
+  return sanala::launch_quant_rows(static_cast<const uint16_t*>(x), rows, C, static_cast<int8_t*>(xq), x_scale,
+                                   stream) == hipSuccess
+             ? SANA_OK
+             : SANA_ERR_HIP;
+}
+
+extern "C" sana_status_t sana_qkv_w8a8_linear_attn_fwd(const void* x, const void* Wt_q, const float* w_scale,
+                                                       const float* gq, const float* gk, int B, int N, int H, int D,
+                                                       float eps, void* out, hipStream_t stream) {
+  if (!x || !Wt_q || !w_scale || !out) return SANA_ERR_INVALID_ARG;
+  sana_status_t st = check_common(B, N, H, D, eps, gq, gk);
+  if (st != SANA_OK) return st;
+  const int64_t C = (int64_t)H * D;
+  if (C % 64 != 0) return SANA_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(Wt_q) || !aligned16(w_scale) || !aligned16(out)) return SANA_ERR_MISALIGNED;
+  const int64_t M = (int64_t)B * N;
+  const size_t xbytes = (size_t)M * C * 2;
+  if (overlaps(out, xbytes, x, xbytes) || overlaps(out, xbytes, Wt_q, (size_t)C * 3 * C) ||
+      overlaps(out, xbytes, w_scale, (size_t)C * 3 * 4))
+    return SANA_ERR_INVALID_ARG;
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SANA_ERR_HIP;
+  init_pool(dev);
+  g_timing.count = 0;
+  const bool norm = gq != nullptr;
+  const sanala::AttnPlan plan = sanala::plan_attn(B, N, H, sanala::kDtypeBf16, norm);
+  // Stream-ordered scratch: int8 x and its row scales, the bf16 qkv, the K row partial sums of squares.
+  const size_t xq_bytes = ((size_t)M * C + 255) / 256 * 256;
+  const size_t sx_bytes = ((size_t)M * 4 + 255) / 256 * 256;
+  const size_t qkv_bytes = ((size_t)M * 3 * C * 2 + 255) / 256 * 256;
+  const int k_parts = norm ? sanala::qkv_gemm_k_parts((int)C) : 0;
+  const size_t ssq_bytes = ((size_t)M * k_parts * 4 + 255) / 256 * 256;
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, xq_bytes + sx_bytes + qkv_bytes + ssq_bytes + plan.ws_bytes, stream) != hipSuccess)
+    return SANA_ERR_HIP;
+  char* base = static_cast<char*>(ws);
+  int8_t* xq = reinterpret_cast<int8_t*>(base);
+  float* sx = reinterpret_cast<float*>(base + xq_bytes);
+  uint16_t* qkv = reinterpret_cast<uint16_t*>(base + xq_bytes + sx_bytes);
+  float* k_ssq = norm ? reinterpret_cast<float*>(base + xq_bytes + sx_bytes + qkv_bytes) : nullptr;
+  hipError_t e = sanala::launch_quant_rows(static_cast<const uint16_t*>(x), M, (int)C, xq, sx, stream);
+  if (e == hipSuccess)
+    e = sanala::launch_qkv_gemm_i8(xq, static_cast<const int8_t*>(Wt_q), sx, w_scale, qkv, M, (int)C, stream, k_ssq);
+  if (e == hipSuccess)
+    e = sanala::launch_attn(plan, qkv, 3 * C, qkv + C, qkv + 2 * C, 3 * C, gq, gk, eps, out, C,
+                            base + xq_bytes + sx_bytes + qkv_bytes + ssq_bytes, stream, k_ssq, k_parts);
+  const hipError_t ef = hipFreeAsync(ws, stream);
+  return (e == hipSuccess && ef == hipSuccess) ? SANA_OK : SANA_ERR_HIP;
+}

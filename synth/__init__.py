@@ -8,9 +8,11 @@ from .gen import (  # noqa: F401
     CONFIGS,
     AttnInputs,
     QkvInputs,
+    W8A8Inputs,
     bf16_round,
     bf16_bits,
     gen_attn,
     gen_config,
     gen_qkv,
+    gen_w8a8,
 )

@@ -14,7 +14,8 @@ are float32 whose values are exactly representable in the storage type, so the
 GPU side can convert them without further rounding and the oracle can widen
 them to float64 exactly.
 
-Tensor ids: q=0, k=1, v=2, gq=3, gk=4, x=5, Wqkv=6, outlier rows=7.
+Tensor ids: q=0, k=1, v=2, gq=3, gk=4, x=5, Wqkv=6, outlier rows=7, int8 weight codes=8,
+weight column scales=9.
 """
 from __future__ import annotations
 
@@ -23,7 +24,7 @@ from typing import Optional
 
 import numpy as np
 
-TID_Q, TID_K, TID_V, TID_GQ, TID_GK, TID_X, TID_W, TID_OUTLIER = range(8)
+TID_Q, TID_K, TID_V, TID_GQ, TID_GK, TID_X, TID_W, TID_OUTLIER, TID_WCODE, TID_WSCALE = range(10)
 
 C_SANA = 2240
 H_SANA = 70
@@ -109,6 +110,29 @@ class QkvInputs:
         return self.x.shape[1]
 
 
+@dataclass
+class W8A8Inputs:
+    """x: float32 [B, N, C] exact in bf16; wt_q: int8 [3C, C] (row n = the C weight codes of output
+    column n); s_w: float32 [3C] column scales; the effective weight is s_w[n] * wt_q[n, c]."""
+    x: np.ndarray
+    wt_q: np.ndarray
+    s_w: np.ndarray
+    gq: Optional[np.ndarray]
+    gk: Optional[np.ndarray]
+    H: int
+    D: int
+    eps: float
+    name: str = ""
+
+    @property
+    def B(self) -> int:
+        return self.x.shape[0]
+
+    @property
+    def N(self) -> int:
+        return self.x.shape[1]
+
+
 def gains(cfg_id: int, C: int, which: int) -> np.ndarray:
     """RMSNorm gains over all C channels: 1 + 0.1*N(0,1), float32, shared by the batch."""
     return (1.0 + 0.1 * _rng(cfg_id, 0, which).standard_normal(C)).astype(np.float32)
@@ -146,6 +170,21 @@ def gen_qkv(cfg_id: int, B: int, N: int, H: int = H_SANA, D: int = D_SANA, eps: 
     w = _store(w_std * _rng(cfg_id, 0, TID_W).standard_normal((C, 3 * C)), "bf16")
     return QkvInputs(np.stack(xs), w, gains(cfg_id, C, TID_GQ), gains(cfg_id, C, TID_GK), H, D, eps,
                      "bf16", name)
+
+
+def gen_w8a8(cfg_id: int, B: int, N: int, H: int = H_SANA, D: int = D_SANA, eps: float = EPS_SANA,
+             w_std: float = 0.02, norm: bool = True, name: str = "") -> W8A8Inputs:
+    """x ~ N(0,1) bf16 [B, N, C]; int8 weight codes drawn directly as integers, N(0, (127/4)^2)
+    rounded and limited to [-127, 127], with column scales w_std * 4/127 * U(0.75, 1.25), so that the
+    effective weight has about the spread of an N(0, w_std^2) Wqkv."""
+    C = H * D
+    xs = [_store(_rng(cfg_id, b, TID_X).standard_normal((N, C)), "bf16") for b in range(B)]
+    codes = np.rint(_rng(cfg_id, 0, TID_WCODE).standard_normal((3 * C, C)) * (127.0 / 4.0))
+    wt_q = np.clip(codes, -127, 127).astype(np.int8)
+    s_w = (w_std * 4.0 / 127.0 * _rng(cfg_id, 0, TID_WSCALE).uniform(0.75, 1.25, 3 * C)).astype(np.float32)
+    gq = gains(cfg_id, C, TID_GQ) if norm else None
+    gk = gains(cfg_id, C, TID_GK) if norm else None
+    return W8A8Inputs(np.stack(xs), wt_q, s_w, gq, gk, H, D, eps, name)
 
 
 # The five SANA-shaped workloads (C = 2240 = 70 heads x 32).

@@ -72,6 +72,34 @@ def test_qkv_rejects(args, status):
     assert lib.sana_qkv_linear_attn_fwd(*args) == status
 
 
+S_ = 0xA000000  # fake w_scale address
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, B_, S_, G1, G2, 1, 8, 70, 32, 1e-6, O, 0), 1),              # null x
+    ((A, B_, 0, G1, G2, 1, 8, 70, 32, 1e-6, O, 0), 1),               # null w_scale
+    ((A, B_, S_, G1, 0, 1, 8, 70, 32, 1e-6, O, 0), 1),               # one gain NULL
+    ((A, B_, S_, G1, G2, 1, 8, 3, 32, 1e-6, O, 0), 2),               # C = 96 not a multiple of 64
+    ((A, B_, S_ + 4, G1, G2, 1, 8, 70, 32, 1e-6, O, 0), 3),          # misaligned w_scale
+    ((A, B_, S_, G1, G2, 1, 8, 70, 32, 1e-6, B_ + 64, 0), 1),        # out overlaps Wt_q
+])
+def test_w8a8_rejects(args, status):
+    lib = sanala.load_library()
+    assert lib.sana_qkv_w8a8_linear_attn_fwd(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 4, 64, B_, S_, 0), 1),                                       # null x
+    ((A, 0, 64, B_, S_, 0), 1),                                       # no rows
+    ((A, 4, 60, B_, S_, 0), 2),                                       # C not a multiple of 8
+    ((A + 8, 4, 64, B_, S_, 0), 3),                                   # misaligned x
+    ((A, 4, 64, A + 32, S_, 0), 1),                                   # xq overlaps x
+])
+def test_quantize_rows_rejects(args, status):
+    lib = sanala.load_library()
+    assert lib.sana_quantize_rows_i8(*args) == status
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     from linear_attention_diffusion_qk_amd import _lib
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
