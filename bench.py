@@ -9,7 +9,7 @@ host cores as a CPU baseline.
 A step is one sana_linear_attn_fwd call over the resident inputs (row statistics, KV state, chunk
 reduction and output: the whole path).
 
-  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload config4|config2|config3|config5]
+  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload config4|config2|config3|config5|w8a8]
   python bench.py --mode copy        # plain device copy of known size (counter calibration under rocprofv3)
   python bench.py --summarize-traffic KERNEL_FETCH.db KERNEL_WRITE.db COPY_FETCH.db COPY_WRITE.db
                                      # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE databases -> profiles/hbm_traffic.txt
@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
+MFMA_I8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA peak
 
 WORKLOADS = {
     "config4": dict(cfg=4, desc="4K linear attention: B=1, N=16384 (128x128 latent), H=70, D=32, bf16 I/O, "
@@ -35,6 +36,8 @@ WORKLOADS = {
     "config2": dict(cfg=2, desc="1024px linear attention: B=1, N=1024 (32x32 latent), H=70, D=32, bf16 I/O, QK-RMSNorm on"),
     "config3": dict(cfg=3, desc="1024px repeat-sampling batch: B=32, N=1024, H=70, D=32, bf16 I/O, QK-RMSNorm on"),
     "config5": dict(cfg=5, desc="2K fused front end: x[4,4096,2240] bf16 @ Wqkv[2240,6720] -> linear attention H=70, D=32"),
+    "w8a8": dict(cfg=5, desc="2K front end in W8A8: x[4,4096,2240] bf16 quantised per token, int8 Wt[6720,2240] "
+                             "with column scales -> linear attention H=70, D=32 on bf16 qkv"),
 }
 
 
@@ -75,17 +78,27 @@ class Inputs:
         self.name = name
         self.spec = WORKLOADS[name]
         t0 = time.time()
-        inp = gen_config(self.spec["cfg"])
+        if name == "w8a8":
+            from synth import gen_w8a8
+            inp = gen_w8a8(self.spec["cfg"], 4, 4096)
+            self.kind = "w8a8"
+        else:
+            inp = gen_config(self.spec["cfg"])
+            self.kind = "qkv" if self.spec["cfg"] == 5 else "attn"
         self.host = inp
-        self.kind = "qkv" if self.spec["cfg"] == 5 else "attn"
         bf = torch.bfloat16
         g = lambda a: torch.from_numpy(a).to("cuda")  # noqa: E731
         if self.kind == "attn":
             self.q, self.k, self.v = (torch.from_numpy(a).to("cuda").to(bf) for a in (inp.q, inp.k, inp.v))
             self.out = torch.empty_like(self.q)
-        else:
+        elif self.kind == "qkv":
             self.x = torch.from_numpy(inp.x).to("cuda").to(bf)
             self.w = torch.from_numpy(inp.w).to("cuda").to(bf)
+            self.out = torch.empty_like(self.x)
+        else:
+            self.x = torch.from_numpy(inp.x).to("cuda").to(bf)
+            self.wt = torch.from_numpy(inp.wt_q).to("cuda")
+            self.sw = torch.from_numpy(inp.s_w).to("cuda")
             self.out = torch.empty_like(self.x)
         self.gq, self.gk = g(inp.gq), g(inp.gk)
         self.B, self.N, self.H, self.D = inp.B, inp.N, inp.H, inp.D
@@ -97,9 +110,12 @@ class Inputs:
         if self.kind == "attn":
             sanala.sana_linear_attn_fwd(self.q, self.k, self.v, self.gq, self.gk, self.B, self.N, self.H, self.D,
                                         self.host.eps, self.out)
-        else:
+        elif self.kind == "qkv":
             sanala.sana_qkv_linear_attn_fwd(self.x, self.w, self.gq, self.gk, self.B, self.N, self.H, self.D,
                                             self.host.eps, self.out)
+        else:
+            sanala.sana_qkv_w8a8_linear_attn_fwd(self.x, self.wt, self.sw, self.gq, self.gk, self.B, self.N, self.H,
+                                                 self.D, self.host.eps, self.out)
 
     def algorithmic_bytes(self) -> int:
         """Read Q, K, V and write O once: 4 * B * N * C * 2 bytes (bf16)."""
@@ -160,8 +176,10 @@ def cpu_baseline(inputs: Inputs, min_seconds: float = 12.0, max_reps: int = 200)
     while True:
         if inputs.kind == "attn":
             oracle.linear_attn(h.q, h.k, h.v, h.gq, h.gk, h.H, h.D, h.eps)
-        else:
+        elif inputs.kind == "qkv":
             oracle.qkv_linear_attn(h.x, h.w, h.gq, h.gk, h.H, h.D, h.eps)
+        else:
+            oracle.qkv_w8a8_linear_attn(h.x, h.wt_q, h.s_w, h.gq, h.gk, h.H, h.D, h.eps)
         reps += 1
         el = time.time() - t0
         if el >= min_seconds or reps >= max_reps:
@@ -274,13 +292,15 @@ def main():
 
     kt = kernel_times(main_in, sanala)
     log(f"[bench] per-kernel (events): " + ", ".join(f"{k}={v * 1e3:.1f}us" for k, v in kt.items()))
-    if main_in.kind == "qkv":
-        gemm_ms = kt.get("qkv_gemm", float("nan"))
+    if main_in.kind in ("qkv", "w8a8"):
+        gname = "qkv_gemm" if main_in.kind == "qkv" else "qkv_gemm_i8"
+        peak = MFMA_BF16_PEAK_TFLOPS if main_in.kind == "qkv" else MFMA_I8_PEAK_TOPS
+        gemm_ms = kt.get(gname, float("nan"))
         flops = 2.0 * tokens * main_in.C * 3 * main_in.C
         ach = flops / (gemm_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "qkv_gemm", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "avg_launch_us": round(gemm_ms * 1e3, 2), "algorithmic_per_launch": flops}
+        roof = {"bound": "mfma", "kernel": gname, "achieved": round(ach, 1), "peak": peak,
+                "unit": "TFLOP/s" if main_in.kind == "qkv" else "TOP/s", "frac": round(ach / peak, 4),
+                "traffic": None, "avg_launch_us": round(gemm_ms * 1e3, 2), "algorithmic_per_launch": flops}
     else:
         dom = max((k for k in kt if main_in.kernel_bytes(k) > 0), key=lambda k: kt[k])
         kb = main_in.kernel_bytes(dom)
@@ -316,7 +336,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "int8 projection, bf16 attention" if main_in.kind == "w8a8" else "bf16",
         "data": "synthetic (seeded N(0,1) inputs of SANA shapes; no trained weights)",
         "config": {"workload": WORKLOADS[args.workload]["desc"], "B": main_in.B, "N": main_in.N, "H": main_in.H,
                    "D": main_in.D, "C": main_in.C, "parallelism": "single GPU"},

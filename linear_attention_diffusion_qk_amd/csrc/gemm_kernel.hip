@@ -312,33 +312,58 @@ int qkv_gemm_k_parts(int C) { return (2 * C - 1) / BN - C / BN + 1; }
 // Per-row symmetric int8 quantisation of bf16 x [M, C] (the dynamic activation half of W8A8): with
 // a = max_c |x[m, c]|, q = clamp(rne(x * (127 / a)), -127, 127) and s_x[m] = a / 127, every step in
 // fp32 with correctly rounded division (a = 0 gives q = 0 and s_x = 0).  One wave per row, 16-byte
-// loads; the second pass over the row re-reads it from cache.
+// loads; rows of up to 64 * kQuantRegUnits units stay in registers between the two passes, longer
+// rows are read a second time.
+constexpr int kQuantRegUnits = 8;
+
+__device__ __forceinline__ float bf16_abs_max(u32x4 w, float m) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+  return m;
+}
+
+__device__ __forceinline__ uint2 quant_unit(u32x4 w, float inv) {
+  uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float v = (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
+    const float qf = fminf(fmaxf(rintf(v * inv), -127.f), 127.f);
+    packed[i >> 2] |= ((uint32_t)(int)qf & 0xffu) << (8 * (i & 3));
+  }
+  return make_uint2(packed[0], packed[1]);
+}
+
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t M, int C,
                                                          int8_t* __restrict__ xq, float* __restrict__ s_x) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= M) return;
   const uint16_t* xr = x + row * C;
+  int8_t* qr = xq + row * C;
   const int units = C / 8;  // 16-byte units of the row
   float amax = 0.f;
-  for (int u = lane; u < units; u += 64) {
-    const u32x4 w = load16(xr + 8 * u);
+  if (units <= 64 * kQuantRegUnits) {
+    u32x4 w[kQuantRegUnits];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-  const float inv = amax > 0.f ? 127.f / amax : 0.f;
-  for (int u = lane; u < units; u += 64) {
-    const u32x4 w = load16(xr + 8 * u);
-    uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float v = (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
-      const float qf = fminf(fmaxf(rintf(v * inv), -127.f), 127.f);
-      packed[i >> 2] |= ((uint32_t)(int)qf & 0xffu) << (8 * (i & 3));
+    for (int j = 0; j < kQuantRegUnits; ++j) {
+      const int u = lane + 64 * j;
+      w[j] = u < units ? load16(xr + 8 * u) : u32x4{0u, 0u, 0u, 0u};
+      amax = bf16_abs_max(w[j], amax);
     }
-    *reinterpret_cast<uint2*>(xq + row * C + 8 * u) = make_uint2(packed[0], packed[1]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const float inv = amax > 0.f ? 127.f / amax : 0.f;
+#pragma unroll
+    for (int j = 0; j < kQuantRegUnits; ++j) {
+      const int u = lane + 64 * j;
+      if (u < units) *reinterpret_cast<uint2*>(qr + 8 * u) = quant_unit(w[j], inv);
+    }
+  } else {
+    for (int u = lane; u < units; u += 64) amax = bf16_abs_max(load16(xr + 8 * u), amax);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const float inv = amax > 0.f ? 127.f / amax : 0.f;
+    for (int u = lane; u < units; u += 64) *reinterpret_cast<uint2*>(qr + 8 * u) = quant_unit(load16(xr + 8 * u), inv);
   }
   if (lane == 0) s_x[row] = amax / 127.f;
 }
