@@ -21,4 +21,5 @@ from .linear_attn import (  # noqa: F401
     rms_inverse,
     split_heads,
 )
+from .mix_ffn import depthwise_conv3x3, expand, glu, mix_ffn  # noqa: F401
 from .w8a8 import qkv_w8a8_linear_attn, quantize_rows, quantize_weight, w8a8_project  # noqa: F401
