@@ -9,7 +9,7 @@ host cores as a CPU baseline.
 A step is one sana_linear_attn_fwd call over the resident inputs (row statistics, KV state, chunk
 reduction and output: the whole path).
 
-  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload config4|config2|config3|config5|w8a8]
+  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload config4|config2|config3|config5|w8a8|mixffn]
   python bench.py --mode copy        # plain device copy of known size (counter calibration under rocprofv3)
   python bench.py --summarize-traffic KERNEL_FETCH.db KERNEL_WRITE.db COPY_FETCH.db COPY_WRITE.db
                                      # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE databases -> profiles/hbm_traffic.txt
@@ -38,6 +38,8 @@ WORKLOADS = {
     "config5": dict(cfg=5, desc="2K fused front end: x[4,4096,2240] bf16 @ Wqkv[2240,6720] -> linear attention H=70, D=32"),
     "w8a8": dict(cfg=5, desc="2K front end in W8A8: x[4,4096,2240] bf16 quantised per token, int8 Wt[6720,2240] "
                              "with column scales -> linear attention H=70, D=32 on bf16 qkv"),
+    "mixffn": dict(cfg=5, desc="2K Mix-FFN: x[4, 64x64, 2240] bf16 @ W1[2240,11200] -> 3x3 depthwise conv (zero pad) "
+                               "-> GLU -> @ W2[5600,2240]"),
 }
 
 
@@ -82,6 +84,10 @@ class Inputs:
             from synth import gen_w8a8
             inp = gen_w8a8(self.spec["cfg"], 4, 4096)
             self.kind = "w8a8"
+        elif name == "mixffn":
+            from synth import gen_mix_ffn
+            inp = gen_mix_ffn(self.spec["cfg"], 4, 64, 64)
+            self.kind = "mixffn"
         else:
             inp = gen_config(self.spec["cfg"])
             self.kind = "qkv" if self.spec["cfg"] == 5 else "attn"
@@ -95,14 +101,22 @@ class Inputs:
             self.x = torch.from_numpy(inp.x).to("cuda").to(bf)
             self.w = torch.from_numpy(inp.w).to("cuda").to(bf)
             self.out = torch.empty_like(self.x)
+        elif self.kind == "mixffn":
+            self.x, self.w1, self.kdw, self.w2 = (torch.from_numpy(a).to("cuda").to(bf)
+                                                  for a in (inp.x, inp.w1, inp.kdw, inp.w2))
+            self.out = torch.empty_like(self.x)
         else:
             self.x = torch.from_numpy(inp.x).to("cuda").to(bf)
             self.wt = torch.from_numpy(inp.wt_q).to("cuda")
             self.sw = torch.from_numpy(inp.s_w).to("cuda")
             self.out = torch.empty_like(self.x)
-        self.gq, self.gk = g(inp.gq), g(inp.gk)
-        self.B, self.N, self.H, self.D = inp.B, inp.N, inp.H, inp.D
-        self.C = self.H * self.D
+        if self.kind == "mixffn":
+            self.B, self.N, self.C = inp.x.shape
+            self.H, self.D = self.C // 32, 32
+        else:
+            self.gq, self.gk = g(inp.gq), g(inp.gk)
+            self.B, self.N, self.H, self.D = inp.B, inp.N, inp.H, inp.D
+            self.C = self.H * self.D
         torch.cuda.synchronize()
         log(f"[bench] {name}: inputs generated and resident in {time.time() - t0:.1f}s")
 
@@ -113,6 +127,9 @@ class Inputs:
         elif self.kind == "qkv":
             sanala.sana_qkv_linear_attn_fwd(self.x, self.w, self.gq, self.gk, self.B, self.N, self.H, self.D,
                                             self.host.eps, self.out)
+        elif self.kind == "mixffn":
+            sanala.sana_mix_ffn_fwd(self.x, self.w1, self.kdw, self.w2, self.B, self.host.Hg, self.host.Wg, self.C,
+                                    self.host.F, self.out)
         else:
             sanala.sana_qkv_w8a8_linear_attn_fwd(self.x, self.wt, self.sw, self.gq, self.gk, self.B, self.N, self.H,
                                                  self.D, self.host.eps, self.out)
@@ -178,6 +195,8 @@ def cpu_baseline(inputs: Inputs, min_seconds: float = 12.0, max_reps: int = 200)
             oracle.linear_attn(h.q, h.k, h.v, h.gq, h.gk, h.H, h.D, h.eps)
         elif inputs.kind == "qkv":
             oracle.qkv_linear_attn(h.x, h.w, h.gq, h.gk, h.H, h.D, h.eps)
+        elif inputs.kind == "mixffn":
+            oracle.mix_ffn(h.x, h.w1, h.kdw, h.w2, h.Hg, h.Wg)
         else:
             oracle.qkv_w8a8_linear_attn(h.x, h.wt_q, h.s_w, h.gq, h.gk, h.H, h.D, h.eps)
         reps += 1
@@ -292,7 +311,20 @@ def main():
 
     kt = kernel_times(main_in, sanala)
     log(f"[bench] per-kernel (events): " + ", ".join(f"{k}={v * 1e3:.1f}us" for k, v in kt.items()))
-    if main_in.kind in ("qkv", "w8a8"):
+    if main_in.kind == "mixffn":
+        F = main_in.host.F
+        gemm_ms = kt.get("gemm_expand", float("nan"))
+        flops = 2.0 * tokens * main_in.C * 2 * F
+        ach = flops / (gemm_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "gemm_expand", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "avg_launch_us": round(gemm_ms * 1e3, 2), "algorithmic_per_launch": flops}
+        cb = tokens * (2 * F + F) * 2
+        conv_ms = kt.get("dwconv_glu", float("nan"))
+        roof["dwconv_glu"] = {"bound": "hbm", "achieved": round(cb / (conv_ms * 1e-3) / 1e9, 1),
+                              "peak": HBM_PEAK_GBPS, "unit": "GB/s", "algorithmic_per_launch": cb,
+                              "avg_launch_us": round(conv_ms * 1e3, 2)}
+    elif main_in.kind in ("qkv", "w8a8"):
         gname = "qkv_gemm" if main_in.kind == "qkv" else "qkv_gemm_i8"
         peak = MFMA_BF16_PEAK_TFLOPS if main_in.kind == "qkv" else MFMA_I8_PEAK_TOPS
         gemm_ms = kt.get(gname, float("nan"))

@@ -116,6 +116,26 @@ sana_status_t sana_qkv_w8a8_linear_attn_fwd(const void* x, const void* Wt_q, con
                                             void* out, hipStream_t stream);
 
 /*
+ * sana_mix_ffn_fwd -- Mix-FFN, the feed-forward half of the Linear DiT block (the Sana notes, section
+ * 2.2: inverted residual block, 3x3 depthwise convolution, GLU; section 2.3: zero padding of that
+ * convolution):  h = x @ W1 (bf16 MFMA GEMM, rounded to bf16); u = 3x3 depthwise cross-correlation
+ * of h over each sample's Hg x Wg token grid with zero padding; g = u[:, :F] * sigmoid(u[:, F:])
+ * (fp32, rounded to bf16); out = g @ W2 (bf16 GEMM).  No biases; the block's residual add is the
+ * caller's.
+ *
+ *   x        device bf16 [B, Hg*Wg, C], tokens in raster order (n = i*Wg + j), 16-byte aligned.
+ *   W1       device bf16 [C, 2F] row-major: columns [0,F) the values, [F,2F) the gates.
+ *   Wdw      device bf16 [2F, 3, 3]: tap (p, q) of channel c reads grid row i+p-1, column j+q-1.
+ *   W2       device bf16 [F, C] row-major.
+ *   B, Hg, Wg  >= 1, Wg <= 128; C and F multiples of 32 (SANA: C = 2240, F = 5600).
+ *   out      device bf16 [B, Hg*Wg, C], 16-byte aligned, not overlapping the inputs; fully overwritten.
+ *
+ * Scratch (stream-ordered): h (B*Hg*Wg*2F bf16) and g (B*Hg*Wg*F bf16).  Errors as above.
+ */
+sana_status_t sana_mix_ffn_fwd(const void* x, const void* W1, const void* Wdw, const void* W2,
+                               int B, int Hg, int Wg, int C, int F, void* out, hipStream_t stream);
+
+/*
  * sana_quantize_rows_i8 -- per-row symmetric int8 quantisation of bf16 x [rows, C] (the activation
  * half of W8A8): with a = max_c |x[r, c]|, xq = clamp(rne(x * (127 / a)), -127, 127) and
  * x_scale[r] = a / 127, each step in fp32 with correctly rounded division; a row of zeros gives

@@ -6,10 +6,12 @@ this package only loads that library and marshals torch tensors into it.
 from ._lib import EXPORTS, SanaError, library_path, load_library, status_string  # noqa: F401
 from .api import (  # noqa: F401
     linear_attn,
+    mix_ffn,
     qkv_linear_attn,
     qkv_w8a8_linear_attn,
     quantize_rows_i8,
     sana_linear_attn_fwd,
+    sana_mix_ffn_fwd,
     sana_qkv_linear_attn_fwd,
     sana_qkv_w8a8_linear_attn_fwd,
     sana_quantize_rows_i8,

@@ -76,6 +76,15 @@ def sana_quantize_rows_i8(x, rows: int, C: int, xq, x_scale, stream=None) -> Non
         raise SanaError(st, "sana_quantize_rows_i8")
 
 
+def sana_mix_ffn_fwd(x, W1, Wdw, W2, B: int, Hg: int, Wg: int, C: int, F: int, out, stream=None) -> None:
+    _check_dev(x, W1, Wdw, W2, out)
+    lib = _lib.load_library()
+    st = lib.sana_mix_ffn_fwd(_ptr(x), _ptr(W1), _ptr(Wdw), _ptr(W2), int(B), int(Hg), int(Wg), int(C), int(F),
+                              _ptr(out), _stream_handle(stream))
+    if st != _lib.SANA_OK:
+        raise SanaError(st, "sana_mix_ffn_fwd")
+
+
 def linear_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gq: Optional[torch.Tensor],
                 gk: Optional[torch.Tensor], H: int, D: int = 32, eps: float = 1e-6,
                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -123,6 +132,21 @@ def qkv_w8a8_linear_attn(x: torch.Tensor, Wt_q: torch.Tensor, w_scale: torch.Ten
     if out is None:
         out = torch.empty_like(x)
     sana_qkv_w8a8_linear_attn_fwd(x, Wt_q, w_scale, gq, gk, B, N, H, D, eps, out)
+    return out
+
+
+def mix_ffn(x: torch.Tensor, W1: torch.Tensor, Wdw: torch.Tensor, W2: torch.Tensor, Hg: int, Wg: int,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x [B, Hg*Wg, C] bf16, W1 [C, 2F], Wdw [2F, 3, 3], W2 [F, C] (all bf16) -> Mix-FFN output [B, Hg*Wg, C]."""
+    if x.dim() != 3 or any(t.dtype != torch.bfloat16 for t in (x, W1, Wdw, W2)):
+        raise ValueError("x, W1, Wdw and W2 must be bf16")
+    B, N, C = x.shape
+    F = W2.shape[0]
+    if N != Hg * Wg or tuple(W1.shape) != (C, 2 * F) or tuple(Wdw.shape) != (2 * F, 3, 3) or tuple(W2.shape) != (F, C):
+        raise ValueError("shape mismatch between x, W1, Wdw, W2 and the grid")
+    if out is None:
+        out = torch.empty_like(x)
+    sana_mix_ffn_fwd(x, W1, Wdw, W2, B, Hg, Wg, C, F, out)
     return out
 
 

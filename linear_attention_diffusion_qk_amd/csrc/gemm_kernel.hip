@@ -387,6 +387,17 @@ hipError_t launch_qkv_gemm(const uint16_t* x, const uint16_t* w, uint16_t* qkv, 
   return hipGetLastError();
 }
 
+hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t M, int K, int NO,
+                            hipStream_t stream, const char* label) {
+  if (K % BK != 0 || NO % 8 != 0 || M > (1LL << 30)) return hipErrorInvalidValue;
+  const int mblocks = (int)((M + BM - 1) / BM), nblocks = (NO + BN - 1) / BN;
+  const int slab = mblocks >= 8 ? (mblocks + 7) / 8 : 0;
+  const int64_t blocks = slab > 0 ? (int64_t)8 * slab * nblocks : (int64_t)mblocks * nblocks;
+  SANA_LAUNCH(label, qkv_gemm_kernel<false><<<(unsigned)blocks, kThreads, 0, stream>>>(
+                          x, w, nullptr, nullptr, y, (int)M, K, NO, mblocks, nblocks, slab, nullptr, 0));
+  return hipGetLastError();
+}
+
 hipError_t launch_qkv_gemm_i8(const int8_t* xq, const int8_t* wt, const float* s_x, const float* s_w, uint16_t* qkv,
                               int64_t M, int C, hipStream_t stream, float* k_ssq) {
   const int NO = 3 * C;

@@ -183,6 +183,32 @@ extern "C" sana_status_t sana_qkv_linear_attn_fwd(const void* x, const void* Wqk
 }
 
 
+extern "C" sana_status_t sana_mix_ffn_fwd(const void* x, const void* W1, const void* Wdw, const void* W2, int B,
+                                          int Hg, int Wg, int C, int F, void* out, hipStream_t stream) {
+  if (!x || !W1 || !Wdw || !W2 || !out) return SANA_ERR_INVALID_ARG;
+  if (B < 1 || Hg < 1 || Wg < 1 || C < 1 || F < 1) return SANA_ERR_INVALID_ARG;
+  if (C % 32 != 0 || F % 32 != 0 || Wg > sanala::mix_ffn_max_width() || B > 65535) return SANA_ERR_UNSUPPORTED;
+  const int64_t M = (int64_t)B * Hg * Wg;
+  if (M > (int64_t(1) << 30) || (double)M * 2.0 * F >= 1099511627776.0) return SANA_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(W1) || !aligned16(W2) || !aligned16(out) || (reinterpret_cast<uintptr_t>(Wdw) & 1))
+    return SANA_ERR_MISALIGNED;
+  const size_t xbytes = (size_t)M * C * 2;
+  if (overlaps(out, xbytes, x, xbytes) || overlaps(out, xbytes, W1, (size_t)C * 2 * F * 2) ||
+      overlaps(out, xbytes, W2, (size_t)F * C * 2) || overlaps(out, xbytes, Wdw, (size_t)2 * F * 9 * 2))
+    return SANA_ERR_INVALID_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SANA_ERR_HIP;
+  init_pool(dev);
+  g_timing.count = 0;
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, sanala::mix_ffn_workspace_bytes(M, F), stream) != hipSuccess) return SANA_ERR_HIP;
+  const hipError_t e = sanala::launch_mix_ffn(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W1),
+                                              static_cast<const uint16_t*>(Wdw), static_cast<const uint16_t*>(W2), B,
+                                              Hg, Wg, C, F, static_cast<uint16_t*>(out), ws, stream);
+  const hipError_t ef = hipFreeAsync(ws, stream);
+  return (e == hipSuccess && ef == hipSuccess) ? SANA_OK : SANA_ERR_HIP;
+}
+
 extern "C" sana_status_t sana_quantize_rows_i8(const void* x, int64_t rows, int C, void* xq, float* x_scale,
                                                hipStream_t stream) {
   if (!x || !xq || !x_scale || rows < 1 || C < 1) return SANA_ERR_INVALID_ARG;

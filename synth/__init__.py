@@ -7,12 +7,14 @@ the GPU side can take their inputs from it without sharing any computation.
 from .gen import (  # noqa: F401
     CONFIGS,
     AttnInputs,
+    MixFfnInputs,
     QkvInputs,
     W8A8Inputs,
     bf16_round,
     bf16_bits,
     gen_attn,
     gen_config,
+    gen_mix_ffn,
     gen_qkv,
     gen_w8a8,
 )

@@ -15,7 +15,7 @@ GPU side can convert them without further rounding and the oracle can widen
 them to float64 exactly.
 
 Tensor ids: q=0, k=1, v=2, gq=3, gk=4, x=5, Wqkv=6, outlier rows=7, int8 weight codes=8,
-weight column scales=9.
+weight column scales=9, Mix-FFN W1=10, depthwise taps=11, W2=12.
 """
 from __future__ import annotations
 
@@ -24,7 +24,8 @@ from typing import Optional
 
 import numpy as np
 
-TID_Q, TID_K, TID_V, TID_GQ, TID_GK, TID_X, TID_W, TID_OUTLIER, TID_WCODE, TID_WSCALE = range(10)
+(TID_Q, TID_K, TID_V, TID_GQ, TID_GK, TID_X, TID_W, TID_OUTLIER, TID_WCODE, TID_WSCALE, TID_W1, TID_KDW,
+ TID_W2) = range(13)
 
 C_SANA = 2240
 H_SANA = 70
@@ -185,6 +186,37 @@ def gen_w8a8(cfg_id: int, B: int, N: int, H: int = H_SANA, D: int = D_SANA, eps:
     gq = gains(cfg_id, C, TID_GQ) if norm else None
     gk = gains(cfg_id, C, TID_GK) if norm else None
     return W8A8Inputs(np.stack(xs), wt_q, s_w, gq, gk, H, D, eps, name)
+
+
+@dataclass
+class MixFfnInputs:
+    """x: float32 [B, Hg*Wg, C]; w1 [C, 2F]; kdw [2F, 3, 3]; w2 [F, C]; all values exact in bf16."""
+    x: np.ndarray
+    w1: np.ndarray
+    kdw: np.ndarray
+    w2: np.ndarray
+    Hg: int
+    Wg: int
+    name: str = ""
+
+    @property
+    def B(self) -> int:
+        return self.x.shape[0]
+
+    @property
+    def F(self) -> int:
+        return self.w2.shape[0]
+
+
+def gen_mix_ffn(cfg_id: int, B: int, Hg: int, Wg: int, C: int = C_SANA, F: int = 5600, w_std: float = 0.02,
+                name: str = "") -> MixFfnInputs:
+    """x ~ N(0,1); W1, W2 ~ N(0, w_std^2); depthwise taps ~ N(0, 1/9); all rounded to bf16."""
+    N = Hg * Wg
+    xs = [_store(_rng(cfg_id, b, TID_X).standard_normal((N, C)), "bf16") for b in range(B)]
+    w1 = _store(w_std * _rng(cfg_id, 0, TID_W1).standard_normal((C, 2 * F)), "bf16")
+    kdw = _store(_rng(cfg_id, 0, TID_KDW).standard_normal((2 * F, 3, 3)) / 3.0, "bf16")
+    w2 = _store(w_std * _rng(cfg_id, 0, TID_W2).standard_normal((F, C)), "bf16")
+    return MixFfnInputs(np.stack(xs), w1, kdw, w2, Hg, Wg, name)
 
 
 # The five SANA-shaped workloads (C = 2240 = 70 heads x 32).

@@ -100,6 +100,19 @@ def test_quantize_rows_rejects(args, status):
     assert lib.sana_quantize_rows_i8(*args) == status
 
 
+@pytest.mark.parametrize("args,status", [
+    ((0, B_, C_, G1, 1, 8, 8, 2240, 5600, O, 0), 1),                 # null x
+    ((A, B_, C_, G1, 0, 8, 8, 2240, 5600, O, 0), 1),                 # B = 0
+    ((A, B_, C_, G1, 1, 8, 8, 2240, 5000, O, 0), 2),                 # F not a multiple of 32
+    ((A, B_, C_, G1, 1, 8, 200, 2240, 5600, O, 0), 2),               # Wg > 128
+    ((A + 2, B_, C_, G1, 1, 8, 8, 2240, 5600, O, 0), 3),             # misaligned x
+    ((A, B_, C_, G1, 1, 8, 8, 2240, 5600, A + 64, 0), 1),            # out overlaps x
+])
+def test_mix_ffn_rejects(args, status):
+    lib = sanala.load_library()
+    assert lib.sana_mix_ffn_fwd(*args) == status
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     from linear_attention_diffusion_qk_amd import _lib
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
