@@ -23,8 +23,12 @@
  * happen on the host before anything is enqueued; faults inside kernels surface at the caller's
  * next synchronisation.  NaN/Inf in the inputs propagate to the outputs they touch; nothing checks
  * for them.  Scratch memory (row statistics, split-N partial states, the reduced state, and for the
- * fused call the qkv buffer) is taken with hipMallocAsync on `stream` and released with
- * hipFreeAsync on the same stream, so concurrent calls on different streams do not share it.
+ * fused calls the qkv buffer) is one buffer per (device, stream), taken from the device's stream-ordered
+ * pool with hipMallocAsync on `stream` the first time and reused by later calls on the same stream
+ * (stream order runs them after the earlier calls' kernels); a call that needs more frees it on
+ * `stream` and takes a larger one.  Calls on different streams never share scratch; calls from several
+ * host threads on one stream are serialised while they enqueue.  The buffers are kept until the process
+ * ends.
  * Results are bitwise reproducible: every reduction runs in a fixed order, with no floating-point
  * atomics.
  */
@@ -86,7 +90,7 @@ sana_status_t sana_linear_attn_fwd(const void* q, const void* k, const void* v,
  *   out      device bf16 [B, N, C]; fully overwritten.
  *   stream   HIP stream.
  *
- * The qkv intermediate (B*N*3C bf16) is stream-ordered scratch.  Errors as above.
+ * The qkv intermediate (B*N*3C bf16) lives in the stream's scratch.  Errors as above.
  */
 sana_status_t sana_qkv_linear_attn_fwd(const void* x, const void* Wqkv,
                                        const float* gq, const float* gk,
@@ -108,7 +112,7 @@ sana_status_t sana_qkv_linear_attn_fwd(const void* x, const void* Wqkv,
  *   gq, gk, B, N, H, D, eps, out, stream as for sana_qkv_linear_attn_fwd; C must be a multiple of 64
  *            (else SANA_ERR_UNSUPPORTED).
  *
- * Scratch (stream-ordered): int8 x, its row scales and the bf16 qkv.  Errors as above.
+ * Scratch (the stream's buffer): int8 x, its row scales and the bf16 qkv.  Errors as above.
  */
 sana_status_t sana_qkv_w8a8_linear_attn_fwd(const void* x, const void* Wt_q, const float* w_scale,
                                             const float* gq, const float* gk,
@@ -130,7 +134,7 @@ sana_status_t sana_qkv_w8a8_linear_attn_fwd(const void* x, const void* Wt_q, con
  *   B, Hg, Wg  >= 1, Wg <= 128; C and F multiples of 32 (SANA: C = 2240, F = 5600).
  *   out      device bf16 [B, Hg*Wg, C], 16-byte aligned, not overlapping the inputs; fully overwritten.
  *
- * Scratch (stream-ordered): h (B*Hg*Wg*2F bf16) and g (B*Hg*Wg*F bf16).  Errors as above.
+ * Scratch (the stream's buffer): h (B*Hg*Wg*2F bf16) and g (B*Hg*Wg*F bf16).  Errors as above.
  */
 sana_status_t sana_mix_ffn_fwd(const void* x, const void* W1, const void* Wdw, const void* W2,
                                int B, int Hg, int Wg, int C, int F, void* out, hipStream_t stream);

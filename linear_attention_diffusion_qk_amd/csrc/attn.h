@@ -14,6 +14,8 @@ constexpr int kDtypeBf16 = 1;
 constexpr int kDtypeF16 = 2;
 constexpr int kOutPersist = 1;  // bf16 output: one block per CU, all heads, operands in LDS
 constexpr int kOutTile = 2;     // bf16 output: 16-token tiles over all heads, operands from global memory
+constexpr int kOutTileGroups = 3;  // bf16 output for few tiles: 16 tokens x 20 heads per block, r_q from the
+                                   // row-statistics launch (which then covers Q and K)
 
 // Launch plan and scratch layout of one attention call.
 struct AttnPlan {
@@ -21,7 +23,7 @@ struct AttnPlan {
   bool norm;
   int Tc;               // tokens per KV chunk (multiple of 64)
   int NC;               // number of chunks per sample
-  int out_kind;         // bf16 output kernel: kOutPersist or kOutTile
+  int out_kind;         // bf16 output kernel: kOutPersist, kOutTile or kOutTileGroups
   bool out_strided;     // persistent output kernel: block b takes tiles b, b + G, ... (else a contiguous run)
   int num_cus;          // compute units of the current device
   size_t off_rk, off_rq, off_part, off_S32, off_z, off_Sop;

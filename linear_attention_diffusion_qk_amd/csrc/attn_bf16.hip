@@ -579,7 +579,12 @@ static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t l
   const unsigned rs_blocks = (unsigned)((rows + 3) / 4);
 
   const float inv_C = 1.0f / (float)C;
-  if (p.norm && k_ssq)
+  float* r_q = reinterpret_cast<float*>(base + p.off_rq);
+  const bool groups = p.out_kind == kOutTileGroups;
+  if (p.norm && groups)  // r_k and r_q in one launch (the output blocks see only some heads of a row)
+    SANA_LAUNCH("rowstats_kq", rowstats_kernel<uint16_t, F16><<<(unsigned)((2 * rows + 3) / 4), 256, 0, stream>>>(
+                                   k, ldkv, rows, C, eps, r_k, q, ldq, r_q));
+  else if (p.norm && k_ssq)
     SANA_LAUNCH("rowfinish_k", rowfinish_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(
                                    k_ssq, k_parts, rows, inv_C, eps, r_k));
   else if (p.norm)
@@ -625,6 +630,17 @@ static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t l
                              q, ldq, gsg, Sop, zop, B, N, H, eps, inv_C, out, ldo, per_arg));
     return hipGetLastError();
   }
+  if (groups) {
+    constexpr int HPWG = 5;  // 20 heads per block
+    const dim3 ogrid((N + 15) / 16, B, (H + 4 * HPWG - 1) / (4 * HPWG));
+    if (p.norm)
+      SANA_LAUNCH("out", out_bf16<HPWG, true, true, F16><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, r_q, N, H,
+                                                                                   eps, inv_C, out, ldo));
+    else
+      SANA_LAUNCH("out", out_bf16<HPWG, false, true, F16><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, nullptr, N,
+                                                                                    H, eps, inv_C, out, ldo));
+    return hipGetLastError();
+  }
   constexpr int HPW = 18;
   if (H <= 4 * HPW) {
     const dim3 ogrid((N + 15) / 16, B, 1);
@@ -636,7 +652,6 @@ static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t l
                                                                                eps, inv_C, out, ldo));
   } else {
     const dim3 ogrid((N + 15) / 16, B, (H + 4 * HPW - 1) / (4 * HPW));
-    float* r_q = reinterpret_cast<float*>(base + p.off_rq);
     if (p.norm) {
       SANA_LAUNCH("rowstats_q", rowstats_kernel<uint16_t, F16><<<rs_blocks, 256, 0, stream>>>(q, ldq, rows, C, eps, r_q));
       SANA_LAUNCH("out", out_bf16<HPW, true, true, F16><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, r_q, N, H, eps,

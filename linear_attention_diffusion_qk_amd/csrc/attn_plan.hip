@@ -46,28 +46,35 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
   const int nc = (int)std::max<int64_t>(1, (1024 + per_chunk - 1) / per_chunk);
   const int n64 = (N + 63) / 64 * 64;
   int Tc = ((N + nc - 1) / nc + 63) / 64 * 64;
-  Tc = std::max(Tc, std::min(256, n64));
+  // Small problems (cache-resident, latency-bound) take 64-token chunks for more blocks.
+  const int min_chunk = (int64_t)B * N <= 8192 ? 64 : 256;
+  Tc = std::max(Tc, std::min(min_chunk, n64));
   Tc = env_int("SANA_KV_CHUNK", Tc);
   Tc = std::max(64, (Tc + 63) / 64 * 64);
   p.Tc = Tc;
   p.NC = (N + Tc - 1) / Tc;
   // bf16 output kernel: persistent when the sample's operands fit in LDS and there are enough tiles to
   // fill the device (SANA_OUT_KERNEL=2 asks for the tile kernel).
-  p.out_kind = (bf && H <= 80 && out_persist_lds_bytes(H) <= kMaxLds &&
-                (int64_t)B * ((N + 15) / 16) >= 2 * p.num_cus && env_int("SANA_OUT_KERNEL", kOutPersist) != kOutTile)
-                   ? kOutPersist
-                   : kOutTile;
+  const int64_t tiles = (int64_t)B * ((N + 15) / 16);
+  const int out_env = env_int("SANA_OUT_KERNEL", 0);
+  if (bf && H <= 80 && out_persist_lds_bytes(H) <= kMaxLds && tiles >= 2 * p.num_cus && out_env != kOutTile &&
+      out_env != kOutTileGroups)
+    p.out_kind = kOutPersist;
+  else if (bf && ((tiles < 2 * p.num_cus && out_env != kOutTile) || out_env == kOutTileGroups))
+    p.out_kind = kOutTileGroups;  // too few tiles for one per CU: split the heads over blocks
+  else
+    p.out_kind = kOutTile;
   // Strided tiles once a sample spans at least two tiles per block (so that a block's tiles stay within
   // few samples); SANA_OUT_SCHED=1 asks for contiguous runs.
   {
-    const int64_t tiles = (int64_t)B * ((N + 15) / 16);
     const int64_t blocks = std::min<int64_t>(p.num_cus, tiles);
     p.out_strided = p.out_kind == kOutPersist && (N + 15) / 16 >= 2 * blocks && env_int("SANA_OUT_SCHED", 2) != 1;
   }
   const size_t BH = (size_t)B * H;
   size_t off = 0;
   p.off_rk = off;   off = align_up(off + (norm ? (size_t)B * N * 4 : 0), 256);
-  p.off_rq = off;   off = align_up(off + (norm && bf && H > 72 ? (size_t)B * N * 4 : 0), 256);
+  p.off_rq = off;
+  off = align_up(off + (norm && bf && (H > 72 || p.out_kind == kOutTileGroups) ? (size_t)B * N * 4 : 0), 256);
   p.off_part = off; off = align_up(off + (p.NC > 1 || !bf ? BH * p.NC * kPartStrideBytes : 0), 256);
   p.off_S32 = off;  off = align_up(off + (bf ? 0 : BH * kHeadDim * kHeadDim * 4), 256);
   p.off_z = off;    off = align_up(off + (bf ? 0 : BH * kHeadDim * 4), 256);

@@ -7,12 +7,22 @@ namespace sanala {
 
 // r[row] = 1 / sqrt(mean_c x[row, c]^2 + eps) over all C channels of a token row (the QK-Norm
 // scale), one wave per row, 16-byte loads (16-bit T: bf16, or binary16 with F16).  Rows are `ld` elements apart.
+// With x1 given, the launch covers 2 * rows rows: the second half are the rows of x1 (stride ld1)
+// and their scales go to r1 (K and Q in one launch).
 template <typename T, bool F16 = false>
 __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ x, int64_t ld, int64_t rows, int C,
-                                                       float eps, float* __restrict__ r) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+                                                       float eps, float* __restrict__ r,
+                                                       const T* __restrict__ x1 = nullptr, int64_t ld1 = 0,
+                                                       float* __restrict__ r1 = nullptr) {
+  int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
+  if (row >= (x1 ? 2 * rows : rows)) return;
+  if (row >= rows) {  // uniform per wave
+    x = x1;
+    ld = ld1;
+    r = r1;
+    row -= rows;
+  }
   const char* p = reinterpret_cast<const char*>(x + row * ld);
   const int nvec = C * (int)sizeof(T) / 16;
   float ss = 0.f;

@@ -223,12 +223,22 @@ def _rowwise_check(o, o_ref, rows, H, label):
             assert err <= 1e-2 * scale + 1e-30, f"{label}: row {b},{n} head {h}: err {err:.3e} vs scale {scale:.3e}"
 
 
-@pytest.mark.parametrize("kind", ["1", "2"])
-def test_output_kernels_agree_with_oracle(gpu_lib, kind):
-    """Persistent (1) and tile (2) output kernels on the same inputs."""
-    inp = gen_attn(41, 2, 2100, dtype="bf16")
+@pytest.mark.parametrize("kind", ["1", "2", "3"])
+@pytest.mark.parametrize("N", [2100, 8200])
+def test_output_kernels_agree_with_oracle(gpu_lib, kind, N):
+    """The output kernels on the same inputs: the default choice (1: persistent at 8200 tokens x 2, head
+    groups at 2100 x 2), the tile kernel over all heads (2) and the head-group kernel with r_q from the
+    row-statistics launch (3)."""
+    inp = gen_attn(41, 2, N, dtype="bf16")
     o = _with_env("SANA_OUT_KERNEL", kind, lambda: run_attn(gpu_lib, inp))
-    check(o, oracle_out(inp), inp.v, "bf16", f"out kernel {kind}")
+    check(o, oracle_out(inp), inp.v, "bf16", f"out kernel {kind} N={N}")
+
+
+def test_many_heads_tile_kernel_with_row_statistics_of_q(gpu_lib):
+    """H = 80 with many tiles: the operands exceed the LDS, so the tile kernel runs over head groups of
+    72 with r_q from a row-statistics pass over Q."""
+    inp = gen_attn(46, 1, 8200, H=80, dtype="bf16")
+    check(run_attn(gpu_lib, inp), oracle_out(inp), inp.v, "bf16", "H=80 N=8200")
 
 
 @pytest.mark.parametrize("B,N,norm", [(1, 12345, True), (2, 8200, True), (1, 9000, False)])
@@ -253,7 +263,7 @@ def test_persistent_schedules_agree(gpu_lib, B, N, norm):
     check(o_strided, oracle_out(inp), inp.v, "bf16", f"schedules B={B} N={N} norm={norm}")
 
 
-@pytest.mark.parametrize("kind", ["1", "2"])
+@pytest.mark.parametrize("kind", ["1", "2", "3"])
 def test_mixed_scale_query_rows(gpu_lib, kind):
     rows = [(0, 3), (0, 64), (1, 100), (1, 4000)]
     inp = _mixed_scale_rows(42, 2, 4100, 70, rows)
