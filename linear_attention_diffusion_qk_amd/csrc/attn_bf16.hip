@@ -78,7 +78,7 @@ __device__ __forceinline__ void emit_state(int64_t bh, int h, int i, float s, co
 // column l%32.  A second MFMA against an all-ones B gives z~ in every column.
 // ---------------------------------------------------------------------------------------------
 template <bool NORM, bool F16>
-__global__ __launch_bounds__(256) void kv_state_bf16(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+__global__ __launch_bounds__(256, 5) void kv_state_bf16(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                      int64_t ld, const float* __restrict__ r_k,
                                                      const float* __restrict__ gq, const float* __restrict__ gk,
                                                      int N, int H, int Tc, int NC, float* __restrict__ part,

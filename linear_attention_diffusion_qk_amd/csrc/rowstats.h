@@ -26,16 +26,39 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ x, 
   const char* p = reinterpret_cast<const char*>(x + row * ld);
   const int nvec = C * (int)sizeof(T) / 16;
   float ss = 0.f;
-  for (int i = lane; i < nvec; i += 64) {
-    const u32x4 w = load16(p + 16 * (int64_t)i);
-    if constexpr (sizeof(T) == 2) {
+  constexpr int MAXU = 8;  // rows of up to 512 units: every load issued before the sums
+  if (nvec <= 64 * MAXU) {
+    u32x4 w[MAXU];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) ss = dot2_h<F16>(w[u], w[u], ss);
-    } else {
+    for (int j = 0; j < MAXU; ++j) {
+      const int i = lane + 64 * j;
+      w[j] = i < nvec ? load16(p + 16 * (int64_t)i) : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float a = __uint_as_float(w[u]);
-        ss = fmaf(a, a, ss);
+    for (int j = 0; j < MAXU; ++j) {
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ss = dot2_h<F16>(w[j][u], w[j][u], ss);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float a = __uint_as_float(w[j][u]);
+          ss = fmaf(a, a, ss);
+        }
+      }
+    }
+  } else {
+    for (int i = lane; i < nvec; i += 64) {
+      const u32x4 w = load16(p + 16 * (int64_t)i);
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ss = dot2_h<F16>(w[u], w[u], ss);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float a = __uint_as_float(w[u]);
+          ss = fmaf(a, a, ss);
+        }
       }
     }
   }
