@@ -39,16 +39,39 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
   p.norm = norm;
   p.num_cus = device_cus();
   const bool bf = dtype != kDtypeF32;  // 16-bit storage: the bf16 / binary16 kernels
-  // KV chunking: about 1024 blocks in total, chunks of at least 256 tokens (the partial state costs
-  // 33/Tc of the K+V traffic), never more than the sequence.
+  // KV chunking.  fp32: about 1024 blocks, chunks of at least 256 tokens (the partial state costs 33/Tc
+  // of the K+V traffic).  16-bit state kernel (block = head pair x chunk, five resident per CU): the
+  // chunk length minimising a cost model fitted to MI355X measurements -- a block streams 256 bytes per
+  // token at about 12 GB/s, a CU at about 23 GB/s, and a split sequence adds the reduction (a launch of
+  // about 6 us plus 0.2 us per chunk).  It picks 14 chunks of 1216 tokens on the 4K workload (73-75 us
+  // per call against 75-77 us for 29 of 576, and 77.8 us for 15 of 1152, whose 525 blocks leave 13 CUs
+  // a third chunk), one chunk per sample for the 32-sample 1024-token batch (no reduction), and 8
+  // chunks of 128 for a single 1024-token sample.
   const int groups = bf ? (H + 1) / 2 : H;
   const int64_t per_chunk = (int64_t)B * groups;
-  const int nc = (int)std::max<int64_t>(1, (1024 + per_chunk - 1) / per_chunk);
   const int n64 = (N + 63) / 64 * 64;
-  int Tc = ((N + nc - 1) / nc + 63) / 64 * 64;
-  // Small problems (cache-resident, latency-bound) take 64-token chunks for more blocks.
-  const int min_chunk = (int64_t)B * N <= 8192 ? 64 : 256;
-  Tc = std::max(Tc, std::min(min_chunk, n64));
+  int Tc;
+  if (bf) {
+    const int min_chunk = std::min(n64, (int64_t)B * N <= 8192 ? 64 : 256);
+    double best = 1e30;
+    Tc = n64;
+    for (int t = min_chunk; t <= n64; t += 64) {
+      const int64_t nc = (N + t - 1) / t;
+      if (t > min_chunk && (N + t - 64 - 1) / (t - 64) == nc) continue;  // same split, shorter chunks
+      const int64_t blocks = per_chunk * nc;
+      const int64_t per_cu = (blocks + p.num_cus - 1) / p.num_cus;
+      const double stream_us = std::max(0.021 * t, 0.0111 * (double)per_cu * t);
+      const double cost = stream_us + (nc > 1 ? 6.0 + 0.2 * (double)nc : 0.0);
+      if (cost < best) {
+        best = cost;
+        Tc = t;
+      }
+    }
+  } else {
+    const int nc = (int)std::max<int64_t>(1, (1024 + per_chunk - 1) / per_chunk);
+    Tc = ((N + nc - 1) / nc + 63) / 64 * 64;
+    Tc = std::max(Tc, std::min(256, n64));
+  }
   Tc = env_int("SANA_KV_CHUNK", Tc);
   Tc = std::max(64, (Tc + 63) / 64 * 64);
   p.Tc = Tc;
