@@ -294,3 +294,29 @@ def test_long_sequences_sampled_rows(gpu_lib, B, N):
     o = run_attn(gpu_lib, inp)
     assert not torch.isnan(o).any()
     _sampled_rows_check(o, inp, f"B={B} N={N}")
+
+
+def test_scratch_reuse_across_streams_and_growth(gpu_lib):
+    """The scratch buffer is kept per stream and grows on demand: interleaved calls on two streams with
+    different sizes, then a larger call on the first stream, each against its own single-stream result."""
+    small = gen_attn(48, 1, 300, dtype="bf16")
+    large = gen_attn(49, 2, 5000, dtype="bf16")
+    ref_small, ref_large = run_attn(gpu_lib, small), run_attn(gpu_lib, large)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    ins = {}
+    for name, inp in (("small", small), ("large", large)):
+        ins[name] = (dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16"), gains_dev(inp.gq), gains_dev(inp.gk))
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(3):
+        for name, stream in (("small", s1), ("large", s2), ("large", s1), ("small", s2)):
+            q, k, v, gq, gk = ins[name]
+            with torch.cuda.stream(stream):
+                out = torch.empty_like(q)
+                gpu_lib.sana_linear_attn_fwd(q, k, v, gq, gk, q.shape[0], q.shape[1], 70, 32, 1e-6, out,
+                                             stream=stream)
+            outs.append((name, out))
+    torch.cuda.synchronize()
+    for name, out in outs:
+        ref = ref_small if name == "small" else ref_large
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), name
