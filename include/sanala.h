@@ -98,6 +98,20 @@ sana_status_t sana_qkv_linear_attn_fwd(const void* x, const void* Wqkv,
                                        void* out, hipStream_t stream);
 
 /*
+ * sana_pack_weight_i8 -- lays out a quantised weight for sana_qkv_w8a8_linear_attn_fwd (done once per
+ * weight, e.g. when a model is loaded).  Wt_q [rows, C] row-major becomes K-blocked: byte
+ * ((c / 64) * rows + n) * 64 + c % 64 of Wt_p holds Wt_q[n, c], so every 64-channel slice of all rows is
+ * one contiguous run.  A pure copy: the codes are not changed.
+ *
+ *   Wt_q     device int8 [rows, C] row-major, 16-byte aligned.
+ *   rows     >= 1, <= 2^30;  C >= 1, a multiple of 64 (else SANA_ERR_UNSUPPORTED).
+ *   Wt_p     device int8, rows * C bytes, 16-byte aligned, not overlapping Wt_q; fully overwritten.
+ *
+ * Returns SANA_OK once enqueued on `stream`; argument errors as above.
+ */
+sana_status_t sana_pack_weight_i8(const void* Wt_q, int64_t rows, int C, void* Wt_p, hipStream_t stream);
+
+/*
  * sana_qkv_w8a8_linear_attn_fwd -- the fused front end with the projection in W8A8 (the Sana notes,
  * section 7: 8-bit weights and activations for deployment, with the linear attention kept in full
  * precision).  x is quantised per token on the device (sana_quantize_rows_i8), the projection runs on
@@ -105,8 +119,9 @@ sana_status_t sana_qkv_linear_attn_fwd(const void* x, const void* Wqkv,
  * (fp32 products in that order), and the attention is that of sana_linear_attn_fwd on bf16 q | k | v.
  *
  *   x        device bf16 [B, N, C], C = H*D, contiguous, 16-byte aligned.
- *   Wt_q     device int8 [3C, C] row-major: the quantised weight transposed, row n holding the C input
- *            weights of output column n (q = rows [0,C), k = [C,2C), v = [2C,3C)); 16-byte aligned.
+ *   Wt_p     device int8, 3C * C bytes: sana_pack_weight_i8(Wt_q, 3C, C, Wt_p) of the quantised weight
+ *            transposed, Wt_q [3C, C], row n holding the C input weights of output column n (q = rows
+ *            [0,C), k = [C,2C), v = [2C,3C)); 16-byte aligned.
  *   w_scale  device fp32 [3C]: dequantisation scale of each output column (W[:, n] ~ w_scale[n] *
  *            Wt_q[n, :]); 16-byte aligned.  The scale granularity is a reading: the pages do not fix it.
  *   gq, gk, B, N, H, D, eps, out, stream as for sana_qkv_linear_attn_fwd; C must be a multiple of 64
@@ -114,7 +129,7 @@ sana_status_t sana_qkv_linear_attn_fwd(const void* x, const void* Wqkv,
  *
  * Scratch (the stream's buffer): int8 x, its row scales and the bf16 qkv.  Errors as above.
  */
-sana_status_t sana_qkv_w8a8_linear_attn_fwd(const void* x, const void* Wt_q, const float* w_scale,
+sana_status_t sana_qkv_w8a8_linear_attn_fwd(const void* x, const void* Wt_p, const float* w_scale,
                                             const float* gq, const float* gk,
                                             int B, int N, int H, int D, float eps,
                                             void* out, hipStream_t stream);

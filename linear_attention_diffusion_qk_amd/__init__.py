@@ -7,11 +7,13 @@ from ._lib import EXPORTS, SanaError, library_path, load_library, status_string 
 from .api import (  # noqa: F401
     linear_attn,
     mix_ffn,
+    pack_weight_i8,
     qkv_linear_attn,
     qkv_w8a8_linear_attn,
     quantize_rows_i8,
     sana_linear_attn_fwd,
     sana_mix_ffn_fwd,
+    sana_pack_weight_i8,
     sana_qkv_linear_attn_fwd,
     sana_qkv_w8a8_linear_attn_fwd,
     sana_quantize_rows_i8,

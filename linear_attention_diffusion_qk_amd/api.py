@@ -65,11 +65,19 @@ def sana_qkv_linear_attn_fwd(x, Wqkv, gq, gk, B: int, N: int, H: int, D: int, ep
         raise SanaError(st, "sana_qkv_linear_attn_fwd")
 
 
-def sana_qkv_w8a8_linear_attn_fwd(x, Wt_q, w_scale, gq, gk, B: int, N: int, H: int, D: int, eps: float, out,
-                                  stream=None) -> None:
-    _check_dev(x, Wt_q, w_scale, gq, gk, out)
+def sana_pack_weight_i8(Wt_q, rows: int, C: int, Wt_p, stream=None) -> None:
+    _check_dev(Wt_q, Wt_p)
     lib = _lib.load_library()
-    st = lib.sana_qkv_w8a8_linear_attn_fwd(_ptr(x), _ptr(Wt_q), _ptr(w_scale), _ptr(gq), _ptr(gk), int(B), int(N),
+    st = lib.sana_pack_weight_i8(_ptr(Wt_q), int(rows), int(C), _ptr(Wt_p), _stream_handle(stream, Wt_q))
+    if st != _lib.SANA_OK:
+        raise SanaError(st, "sana_pack_weight_i8")
+
+
+def sana_qkv_w8a8_linear_attn_fwd(x, Wt_p, w_scale, gq, gk, B: int, N: int, H: int, D: int, eps: float, out,
+                                  stream=None) -> None:
+    _check_dev(x, Wt_p, w_scale, gq, gk, out)
+    lib = _lib.load_library()
+    st = lib.sana_qkv_w8a8_linear_attn_fwd(_ptr(x), _ptr(Wt_p), _ptr(w_scale), _ptr(gq), _ptr(gk), int(B), int(N),
                                            int(H), int(D), float(eps), _ptr(out), _stream_handle(stream, x))
     if st != _lib.SANA_OK:
         raise SanaError(st, "sana_qkv_w8a8_linear_attn_fwd")
@@ -126,19 +134,31 @@ def qkv_linear_attn(x: torch.Tensor, Wqkv: torch.Tensor, gq: Optional[torch.Tens
     return out
 
 
-def qkv_w8a8_linear_attn(x: torch.Tensor, Wt_q: torch.Tensor, w_scale: torch.Tensor, gq: Optional[torch.Tensor],
+def pack_weight_i8(Wt_q: torch.Tensor) -> torch.Tensor:
+    """int8 Wt_q [rows, C] (C a multiple of 64) -> its K-blocked copy [C/64, rows, 64], the weight layout
+    qkv_w8a8_linear_attn takes (packed once per weight)."""
+    if Wt_q.dim() != 2 or Wt_q.dtype != torch.int8 or Wt_q.shape[1] % 64 != 0 or not Wt_q.is_contiguous():
+        raise ValueError("Wt_q must be a contiguous int8 [rows, C] tensor with C a multiple of 64")
+    rows, C = Wt_q.shape
+    Wt_p = torch.empty((C // 64, rows, 64), dtype=torch.int8, device=Wt_q.device)
+    sana_pack_weight_i8(Wt_q, rows, C, Wt_p)
+    return Wt_p
+
+
+def qkv_w8a8_linear_attn(x: torch.Tensor, Wt_p: torch.Tensor, w_scale: torch.Tensor, gq: Optional[torch.Tensor],
                          gk: Optional[torch.Tensor], H: int, D: int = 32, eps: float = 1e-6,
                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """x [B, N, C] bf16, Wt_q [3C, C] int8 (W transposed, quantised per output column), w_scale [3C] fp32
-    -> linear attention of the W8A8 projection's q | k | v blocks (x quantised per token inside)."""
-    if x.dim() != 3 or x.dtype != torch.bfloat16 or Wt_q.dtype != torch.int8 or w_scale.dtype != torch.float32:
-        raise ValueError("x must be bf16 [B, N, C], Wt_q int8 [3C, C] and w_scale float32 [3C]")
+    """x [B, N, C] bf16, Wt_p = pack_weight_i8(Wt_q) [C/64, 3C, 64] int8 (Wt_q [3C, C]: W transposed, quantised
+    per output column), w_scale [3C] fp32 -> linear attention of the W8A8 projection's q | k | v blocks
+    (x quantised per token inside)."""
+    if x.dim() != 3 or x.dtype != torch.bfloat16 or Wt_p.dtype != torch.int8 or w_scale.dtype != torch.float32:
+        raise ValueError("x must be bf16 [B, N, C], Wt_p int8 [C/64, 3C, 64] and w_scale float32 [3C]")
     B, N, C = x.shape
-    if C != H * D or tuple(Wt_q.shape) != (3 * C, C) or w_scale.numel() != 3 * C:
-        raise ValueError("shape mismatch between x, Wt_q, w_scale and H*D")
+    if C != H * D or C % 64 != 0 or tuple(Wt_p.shape) != (C // 64, 3 * C, 64) or w_scale.numel() != 3 * C:
+        raise ValueError("shape mismatch between x, Wt_p, w_scale and H*D")
     if out is None:
         out = torch.empty_like(x)
-    sana_qkv_w8a8_linear_attn_fwd(x, Wt_q, w_scale, gq, gk, B, N, H, D, eps, out)
+    sana_qkv_w8a8_linear_attn_fwd(x, Wt_p, w_scale, gq, gk, B, N, H, D, eps, out)
     return out
 
 

@@ -58,8 +58,9 @@ int max_heads();
 hipError_t launch_qkv_gemm(const uint16_t* x, const uint16_t* w, uint16_t* qkv, int64_t M, int C, hipStream_t stream,
                            float* k_ssq = nullptr);
 int qkv_gemm_k_parts(int C);
-// W8A8 form: xq int8 [M, C] with per-row scales s_x [M]; wt int8 [3C, C] (W transposed: K contiguous
-// per output column) with per-column scales s_w [3C]; qkv = bf16((sum_c xq*wt) * s_x[m] * s_w[n]).
+// W8A8 form: xq int8 K-blocked [C/64][M][64] (launch_quant_rows with k_blocked) with per-row scales
+// s_x [M]; wt int8 K-blocked [C/64][3C][64] (launch_pack_k64 of W transposed, [3C, C]) with per-column
+// scales s_w [3C]; qkv = bf16((sum_c xq*wt) * s_x[m] * s_w[n]).
 // C must be a multiple of 64.  k_ssq as for launch_qkv_gemm.
 hipError_t launch_qkv_gemm_i8(const int8_t* xq, const int8_t* wt, const float* s_x, const float* s_w, uint16_t* qkv,
                               int64_t M, int C, hipStream_t stream, float* k_ssq = nullptr);
@@ -72,8 +73,13 @@ hipError_t launch_mix_ffn(const uint16_t* x, const uint16_t* w1, const uint16_t*
                           int Wg, int C, int F, uint16_t* out, void* ws, hipStream_t stream);
 size_t mix_ffn_workspace_bytes(int64_t M, int F);
 int mix_ffn_max_width();
-// Per-row symmetric int8 quantisation of bf16 x [M, C] (C a multiple of 8).
-hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int C, int8_t* xq, float* s_x, hipStream_t stream);
+// int8 [rows, C] row-major -> K-blocked [C/64][rows][64] (C a multiple of 64).
+hipError_t launch_pack_k64(const int8_t* src, int64_t rows, int C, int8_t* dst, hipStream_t stream);
+
+// Per-row symmetric int8 quantisation of bf16 x [M, C] (C a multiple of 8); codes row-major, or
+// K-blocked [C/64][M][64] for the int8 GEMM (C a multiple of 64).
+hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int C, int8_t* xq, float* s_x, hipStream_t stream,
+                             bool k_blocked = false);
 
 // Measurement hooks (no-ops unless timing is enabled on the calling host thread): an event pair is
 // recorded on `s` around each kernel launch.

@@ -133,7 +133,8 @@ __device__ __forceinline__ void mma(const Ops& op, int s, Acc (&acc)[3][4]) {
 }
 }  // namespace
 
-// x: bf16 [M, K] (I8: int8 [M, K]); w: bf16 [K, NO] (I8: int8 Wt [NO, K]); s_x [M] and s_w [NO]: I8 only.
+// x: bf16 [M, K] (I8: int8, K-blocked: [K/64][M][64]); w: bf16 [K, NO] (I8: int8 Wt, K-blocked:
+// [K/64][NO][64]); s_x [M] and s_w [NO]: I8 only.
 template <bool I8>
 __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const void* __restrict__ x, const void* __restrict__ w,
                                                             const float* __restrict__ s_x,
@@ -162,7 +163,8 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const void* __restri
 
   // Per-lane sources of this wave's DMA instructions (the K step is added per stage).  A instruction
   // i covers rows 16i..16i+15 of the x image, B instruction i bytes [1024i, 1024i + 1024) of the W
-  // image (I8: rows 16i..16i+15 of the Wt image, placed like x).  Rows past M and columns past NO read
+  // image (I8: rows 16i..16i+15 of the Wt image, placed like x; both operands K-blocked, so each
+  // instruction reads one contiguous 1 KB run).  Rows past M and columns past NO read
   // clamped addresses; their products are never stored.
   const char* a_src[A_DMA];
   const char* b_src[B_DMA];
@@ -170,14 +172,17 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const void* __restri
   for (int a = 0; a < A_DMA; ++a) {
     const int r = 16 * (wave * A_DMA + a) + (lane >> 2);
     const int kc = (lane & 3) ^ xswz(r);
-    a_src[a] = xb + (int64_t)min(m0 + r, M - 1) * K * kElem + 16 * kc;
+    // I8: x arrives K-blocked (64-byte slabs, slab t holding row m at byte (t*M + m)*64), so the 16 rows
+    // of one instruction are one contiguous 1 KB run.
+    a_src[a] = I8 ? xb + (int64_t)min(m0 + r, M - 1) * A_ROW + 16 * kc
+                  : xb + (int64_t)min(m0 + r, M - 1) * K * kElem + 16 * kc;
   }
 #pragma unroll
   for (int b = 0; b < B_DMA; ++b) {
     if (I8) {
       const int r = 16 * (wave * B_DMA + b) + (lane >> 2);
       const int kc = (lane & 3) ^ xswz(r);
-      b_src[b] = wbp + (int64_t)min(n0 + r, NO - 1) * K + 16 * kc;
+      b_src[b] = wbp + (int64_t)min(n0 + r, NO - 1) * A_ROW + 16 * kc;
     } else {
       const int off = 1024 * (wave * B_DMA + b) + 16 * lane;
       const int k = off / B_ROW, c = (off % B_ROW) / 16;
@@ -192,11 +197,12 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const void* __restri
     const int tt = min(t, KT - 1);
 #pragma unroll
     for (int a = 0; a < A_DMA; ++a)
-      __builtin_amdgcn_global_load_lds(a_src[a] + tt * A_ROW, (lds_ptr_t)(base + 1024 * (wave * A_DMA + a)), 16, 0,
+      __builtin_amdgcn_global_load_lds(a_src[a] + (I8 ? (int64_t)tt * M * A_ROW : (int64_t)tt * A_ROW),
+                                       (lds_ptr_t)(base + 1024 * (wave * A_DMA + a)), 16, 0,
                                        0);
 #pragma unroll
     for (int b = 0; b < B_DMA; ++b)
-      __builtin_amdgcn_global_load_lds(b_src[b] + (I8 ? (int64_t)tt * A_ROW : (int64_t)tt * BK * NO * 2),
+      __builtin_amdgcn_global_load_lds(b_src[b] + (I8 ? (int64_t)tt * NO * A_ROW : (int64_t)tt * BK * NO * 2),
                                        (lds_ptr_t)(base + A_BYTES + 1024 * (wave * B_DMA + b)), 16, 0, 0);
   };
 
@@ -333,14 +339,20 @@ __device__ __forceinline__ uint2 quant_unit(u32x4 w, float inv) {
   return make_uint2(packed[0], packed[1]);
 }
 
+// BLOCKED: codes stored K-blocked for the int8 GEMM, [C/64][M][64] (the 8 codes of unit u of row m at
+// byte ((8u / 64) * M + m) * 64 + 8u % 64); else row-major [M][C].
+template <bool BLOCKED>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t M, int C,
                                                          int8_t* __restrict__ xq, float* __restrict__ s_x) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= M) return;
   const uint16_t* xr = x + row * C;
-  int8_t* qr = xq + row * C;
   const int units = C / 8;  // 16-byte units of the row
+  auto dst = [&](int u) -> uint2* {
+    return reinterpret_cast<uint2*>(BLOCKED ? xq + ((int64_t)(u >> 3) * M + row) * 64 + 8 * (u & 7)
+                                            : xq + row * C + 8 * u);
+  };
   float amax = 0.f;
   if (units <= 64 * kQuantRegUnits) {
     u32x4 w[kQuantRegUnits];
@@ -356,21 +368,44 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
 #pragma unroll
     for (int j = 0; j < kQuantRegUnits; ++j) {
       const int u = lane + 64 * j;
-      if (u < units) *reinterpret_cast<uint2*>(qr + 8 * u) = quant_unit(w[j], inv);
+      if (u < units) *dst(u) = quant_unit(w[j], inv);
     }
   } else {
     for (int u = lane; u < units; u += 64) amax = bf16_abs_max(load16(xr + 8 * u), amax);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
     const float inv = amax > 0.f ? 127.f / amax : 0.f;
-    for (int u = lane; u < units; u += 64) *reinterpret_cast<uint2*>(qr + 8 * u) = quant_unit(load16(xr + 8 * u), inv);
+    for (int u = lane; u < units; u += 64) *dst(u) = quant_unit(load16(xr + 8 * u), inv);
   }
   if (lane == 0) s_x[row] = amax / 127.f;
 }
 
-hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int C, int8_t* xq, float* s_x, hipStream_t stream) {
-  if (C % 8 != 0) return hipErrorInvalidValue;
-  SANA_LAUNCH("quant_rows", quant_rows_kernel<<<(unsigned)((M + 3) / 4), 256, 0, stream>>>(x, M, C, xq, s_x));
+hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int C, int8_t* xq, float* s_x, hipStream_t stream,
+                             bool k_blocked) {
+  if (C % 8 != 0 || (k_blocked && C % 64 != 0)) return hipErrorInvalidValue;
+  if (k_blocked)
+    SANA_LAUNCH("quant_rows", quant_rows_kernel<true><<<(unsigned)((M + 3) / 4), 256, 0, stream>>>(x, M, C, xq, s_x));
+  else
+    SANA_LAUNCH("quant_rows", quant_rows_kernel<false><<<(unsigned)((M + 3) / 4), 256, 0, stream>>>(x, M, C, xq, s_x));
+  return hipGetLastError();
+}
+
+// One thread per 16-byte unit u of row n: src[n][16u..16u+15] -> dst[u/4][n][16(u%4)..].
+__global__ __launch_bounds__(256) void pack_k64_kernel(const int8_t* __restrict__ src, int64_t rows, int C,
+                                                       int8_t* __restrict__ dst) {
+  const int upr = C / 16;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * upr) return;
+  const int64_t n = i / upr;
+  const int u = (int)(i - n * upr);
+  *reinterpret_cast<u32x4*>(dst + ((int64_t)(u >> 2) * rows + n) * 64 + 16 * (u & 3)) =
+      *reinterpret_cast<const u32x4*>(src + n * C + 16 * u);
+}
+
+hipError_t launch_pack_k64(const int8_t* src, int64_t rows, int C, int8_t* dst, hipStream_t stream) {
+  if (C % 64 != 0) return hipErrorInvalidValue;
+  const int64_t units = rows * (C / 16);
+  SANA_LAUNCH("pack_k64", pack_k64_kernel<<<(unsigned)((units + 255) / 256), 256, 0, stream>>>(src, rows, C, dst));
   return hipGetLastError();
 }
 

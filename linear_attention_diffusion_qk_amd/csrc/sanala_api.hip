@@ -292,18 +292,33 @@ extern "C" sana_status_t sana_quantize_rows_i8(const void* x, int64_t rows, int 
              : SANA_ERR_HIP;
 }
 
-extern "C" sana_status_t sana_qkv_w8a8_linear_attn_fwd(const void* x, const void* Wt_q, const float* w_scale,
+extern "C" sana_status_t sana_pack_weight_i8(const void* Wt_q, int64_t rows, int C, void* Wt_p, hipStream_t stream) {
+  if (!Wt_q || !Wt_p || rows < 1 || C < 1) return SANA_ERR_INVALID_ARG;
+  if (C % 64 != 0 || rows > (int64_t(1) << 30)) return SANA_ERR_UNSUPPORTED;
+  if (!aligned16(Wt_q) || !aligned16(Wt_p)) return SANA_ERR_MISALIGNED;
+  const size_t bytes = (size_t)rows * C;
+  if (overlaps(Wt_p, bytes, Wt_q, bytes)) return SANA_ERR_INVALID_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SANA_ERR_HIP;
+  g_timing.count = 0;
+  return sanala::launch_pack_k64(static_cast<const int8_t*>(Wt_q), rows, C, static_cast<int8_t*>(Wt_p), stream) ==
+                 hipSuccess
+             ? SANA_OK
+             : SANA_ERR_HIP;
+}
+
+extern "C" sana_status_t sana_qkv_w8a8_linear_attn_fwd(const void* x, const void* Wt_p, const float* w_scale,
                                                        const float* gq, const float* gk, int B, int N, int H, int D,
                                                        float eps, void* out, hipStream_t stream) {
-  if (!x || !Wt_q || !w_scale || !out) return SANA_ERR_INVALID_ARG;
+  if (!x || !Wt_p || !w_scale || !out) return SANA_ERR_INVALID_ARG;
   sana_status_t st = check_common(B, N, H, D, eps, gq, gk);
   if (st != SANA_OK) return st;
   const int64_t C = (int64_t)H * D;
   if (C % 64 != 0) return SANA_ERR_UNSUPPORTED;
-  if (!aligned16(x) || !aligned16(Wt_q) || !aligned16(w_scale) || !aligned16(out)) return SANA_ERR_MISALIGNED;
+  if (!aligned16(x) || !aligned16(Wt_p) || !aligned16(w_scale) || !aligned16(out)) return SANA_ERR_MISALIGNED;
   const int64_t M = (int64_t)B * N;
   const size_t xbytes = (size_t)M * C * 2;
-  if (overlaps(out, xbytes, x, xbytes) || overlaps(out, xbytes, Wt_q, (size_t)C * 3 * C) ||
+  if (overlaps(out, xbytes, x, xbytes) || overlaps(out, xbytes, Wt_p, (size_t)C * 3 * C) ||
       overlaps(out, xbytes, w_scale, (size_t)C * 3 * 4))
     return SANA_ERR_INVALID_ARG;
 
@@ -327,9 +342,9 @@ extern "C" sana_status_t sana_qkv_w8a8_linear_attn_fwd(const void* x, const void
   float* sx = reinterpret_cast<float*>(base + xq_bytes);
   uint16_t* qkv = reinterpret_cast<uint16_t*>(base + xq_bytes + sx_bytes);
   float* k_ssq = norm ? reinterpret_cast<float*>(base + xq_bytes + sx_bytes + qkv_bytes) : nullptr;
-  hipError_t e = sanala::launch_quant_rows(static_cast<const uint16_t*>(x), M, (int)C, xq, sx, stream);
+  hipError_t e = sanala::launch_quant_rows(static_cast<const uint16_t*>(x), M, (int)C, xq, sx, stream, true);
   if (e == hipSuccess)
-    e = sanala::launch_qkv_gemm_i8(xq, static_cast<const int8_t*>(Wt_q), sx, w_scale, qkv, M, (int)C, stream, k_ssq);
+    e = sanala::launch_qkv_gemm_i8(xq, static_cast<const int8_t*>(Wt_p), sx, w_scale, qkv, M, (int)C, stream, k_ssq);
   if (e == hipSuccess)
     e = sanala::launch_attn(plan, qkv, 3 * C, qkv + C, qkv + 2 * C, 3 * C, gq, gk, eps, out, C,
                             base + xq_bytes + sx_bytes + qkv_bytes + ssq_bytes, stream, k_ssq, k_parts);

@@ -81,7 +81,7 @@ S_ = 0xA000000  # fake w_scale address
     ((A, B_, S_, G1, 0, 1, 8, 70, 32, 1e-6, O, 0), 1),               # one gain NULL
     ((A, B_, S_, G1, G2, 1, 8, 3, 32, 1e-6, O, 0), 2),               # C = 96 not a multiple of 64
     ((A, B_, S_ + 4, G1, G2, 1, 8, 70, 32, 1e-6, O, 0), 3),          # misaligned w_scale
-    ((A, B_, S_, G1, G2, 1, 8, 70, 32, 1e-6, B_ + 64, 0), 1),        # out overlaps Wt_q
+    ((A, B_, S_, G1, G2, 1, 8, 70, 32, 1e-6, B_ + 64, 0), 1),        # out overlaps Wt_p
 ])
 def test_w8a8_rejects(args, status):
     lib = sanala.load_library()
@@ -98,6 +98,19 @@ def test_w8a8_rejects(args, status):
 def test_quantize_rows_rejects(args, status):
     lib = sanala.load_library()
     assert lib.sana_quantize_rows_i8(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 4, 64, B_, 0), 1),                                           # null Wt_q
+    ((A, 0, 64, B_, 0), 1),                                           # no rows
+    ((A, 4, 96, B_, 0), 2),                                           # C not a multiple of 64
+    ((A, (1 << 30) + 1, 64, B_, 0), 2),                               # too many rows
+    ((A + 8, 4, 64, B_, 0), 3),                                       # misaligned Wt_q
+    ((A, 4, 64, A + 64, 0), 1),                                       # Wt_p overlaps Wt_q
+])
+def test_pack_weight_rejects(args, status):
+    lib = sanala.load_library()
+    assert lib.sana_pack_weight_i8(*args) == status
 
 
 @pytest.mark.parametrize("args,status", [

@@ -21,9 +21,22 @@ def _run(gpu_lib, inp):
     wt = torch.from_numpy(np.ascontiguousarray(inp.wt_q)).to("cuda")
     sw = torch.from_numpy(np.ascontiguousarray(inp.s_w)).to("cuda")
     out = torch.full(x.shape, float("nan"), device="cuda", dtype=torch.bfloat16)
-    o = gpu_lib.qkv_w8a8_linear_attn(x, wt, sw, gains_dev(inp.gq), gains_dev(inp.gk), inp.H, inp.D, inp.eps, out=out)
+    o = gpu_lib.qkv_w8a8_linear_attn(x, gpu_lib.pack_weight_i8(wt), sw, gains_dev(inp.gq), gains_dev(inp.gk), inp.H,
+                                     inp.D, inp.eps, out=out)
     torch.cuda.synchronize()
     return o
+
+
+@pytest.mark.parametrize("rows,C", [(1, 64), (6720, 2240), (13, 192), (300, 4480)])
+def test_pack_weight_layout(gpu_lib, rows, C):
+    """The packed weight against the layout written out: byte ((c // 64) * rows + n) * 64 + c % 64 = Wt[n, c]."""
+    rng = np.random.default_rng(rows + C)
+    wt = rng.integers(-127, 128, size=(rows, C), dtype=np.int8)
+    wp = gpu_lib.pack_weight_i8(torch.from_numpy(wt).to("cuda"))
+    torch.cuda.synchronize()
+    flat = wp.cpu().numpy().reshape(-1)
+    n, c = np.meshgrid(np.arange(rows), np.arange(C), indexing="ij")
+    assert np.array_equal(flat[((c // 64) * rows + n) * 64 + c % 64], wt)
 
 
 @pytest.mark.parametrize("rows,C", [(1, 2240), (37, 2240), (1000, 64), (5, 8), (300, 4480)])
@@ -74,9 +87,12 @@ def test_w8a8_2k_workload_sampled_rows(gpu_lib):
 def test_w8a8_argument_errors(gpu_lib):
     inp = gen_w8a8(9, 1, 16, H=3)                    # C = 96: not a multiple of 64
     x = dev(inp.x, "bf16")
-    wt = torch.from_numpy(np.ascontiguousarray(inp.wt_q)).to("cuda")
+    wt = torch.from_numpy(np.ascontiguousarray(inp.wt_q)).to("cuda")   # layout never read: the calls are rejected
     sw = torch.from_numpy(np.ascontiguousarray(inp.s_w)).to("cuda")
     out = torch.empty_like(x)
+    with pytest.raises(gpu_lib.SanaError) as e:
+        gpu_lib.sana_pack_weight_i8(wt, 9 * 32, 96, torch.empty_like(wt))
+    assert e.value.status == 2
     with pytest.raises(gpu_lib.SanaError) as e:
         gpu_lib.sana_qkv_w8a8_linear_attn_fwd(x, wt, sw, gains_dev(inp.gq), gains_dev(inp.gk), 1, 16, 3, 32, 1e-6, out)
     assert e.value.status == 2
