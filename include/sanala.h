@@ -104,7 +104,7 @@ sana_status_t sana_qkv_linear_attn_fwd(const void* x, const void* Wqkv,
  * one contiguous run.  A pure copy: the codes are not changed.
  *
  *   Wt_q     device int8 [rows, C] row-major, 16-byte aligned.
- *   rows     >= 1, <= 2^30;  C >= 1, a multiple of 64 (else SANA_ERR_UNSUPPORTED).
+ *   rows     >= 1, <= 2^30;  C >= 1, a multiple of 64;  rows * C <= 2^40 (else SANA_ERR_UNSUPPORTED).
  *   Wt_p     device int8, rows * C bytes, 16-byte aligned, not overlapping Wt_q; fully overwritten.
  *
  * Returns SANA_OK once enqueued on `stream`; argument errors as above.

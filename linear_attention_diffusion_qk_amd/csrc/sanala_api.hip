@@ -294,7 +294,7 @@ extern "C" sana_status_t sana_quantize_rows_i8(const void* x, int64_t rows, int 
 
 extern "C" sana_status_t sana_pack_weight_i8(const void* Wt_q, int64_t rows, int C, void* Wt_p, hipStream_t stream) {
   if (!Wt_q || !Wt_p || rows < 1 || C < 1) return SANA_ERR_INVALID_ARG;
-  if (C % 64 != 0 || rows > (int64_t(1) << 30)) return SANA_ERR_UNSUPPORTED;
+  if (C % 64 != 0 || rows > (int64_t(1) << 30) || rows * C > (int64_t(1) << 40)) return SANA_ERR_UNSUPPORTED;
   if (!aligned16(Wt_q) || !aligned16(Wt_p)) return SANA_ERR_MISALIGNED;
   const size_t bytes = (size_t)rows * C;
   if (overlaps(Wt_p, bytes, Wt_q, bytes)) return SANA_ERR_INVALID_ARG;

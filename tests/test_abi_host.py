@@ -105,6 +105,7 @@ def test_quantize_rows_rejects(args, status):
     ((A, 0, 64, B_, 0), 1),                                           # no rows
     ((A, 4, 96, B_, 0), 2),                                           # C not a multiple of 64
     ((A, (1 << 30) + 1, 64, B_, 0), 2),                               # too many rows
+    ((A, 1 << 30, 1 << 11, B_, 0), 2),                                # rows * C > 2^40
     ((A + 8, 4, 64, B_, 0), 3),                                       # misaligned Wt_q
     ((A, 4, 64, A + 64, 0), 1),                                       # Wt_p overlaps Wt_q
 ])
