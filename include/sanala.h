@@ -146,7 +146,7 @@ sana_status_t sana_qkv_w8a8_linear_attn_fwd(const void* x, const void* Wt_p, con
  *   W1       device bf16 [C, 2F] row-major: columns [0,F) the values, [F,2F) the gates.
  *   Wdw      device bf16 [2F, 3, 3]: tap (p, q) of channel c reads grid row i+p-1, column j+q-1.
  *   W2       device bf16 [F, C] row-major.
- *   B, Hg, Wg  >= 1, Wg <= 128; C and F multiples of 32 (SANA: C = 2240, F = 5600).
+ *   B, Hg, Wg  >= 1, Wg <= 128; C and F multiples of 32, at most 2^20 (SANA: C = 2240, F = 5600).
  *   out      device bf16 [B, Hg*Wg, C], 16-byte aligned, not overlapping the inputs; fully overwritten.
  *
  * Scratch (the stream's buffer): h (B*Hg*Wg*2F bf16) and g (B*Hg*Wg*F bf16).  Errors as above.

@@ -52,11 +52,15 @@ size_t bf16_operand_bytes(int64_t BH, int H);
 
 int max_heads();
 
-// qkv[M, 3C] = x[M, C] @ w[C, 3C], bf16 in / bf16 out (fp32 accumulation).  With k_ssq set, the blocks
+// x [M][K] bf16 row-major -> xb [K/32][M][32], the K-blocked x layout the bf16 GEMMs below take
+// (K a multiple of 32).
+hipError_t launch_relayout_k32(const uint16_t* x, int64_t M, int K, uint16_t* xb, hipStream_t stream);
+// qkv[M, 3C] = x[M, C] @ w[C, 3C], bf16 in / bf16 out (fp32 accumulation); xb is x K-blocked
+// (launch_relayout_k32), w row-major.  With k_ssq set, the blocks
 // whose columns overlap the K block [C, 2C) also write, per row, the sum of squares of the bf16 outputs
 // they hold in that block: k_ssq[m * qkv_gemm_k_parts(C) + j] for the j-th such column panel.
-hipError_t launch_qkv_gemm(const uint16_t* x, const uint16_t* w, uint16_t* qkv, int64_t M, int C, hipStream_t stream,
-                           float* k_ssq = nullptr);
+hipError_t launch_qkv_gemm(const uint16_t* xb, const uint16_t* w, uint16_t* qkv, int64_t M, int C,
+                           hipStream_t stream, float* k_ssq = nullptr);
 int qkv_gemm_k_parts(int C);
 // W8A8 form: xq int8 K-blocked [C/64][M][64] (launch_quant_rows with k_blocked) with per-row scales
 // s_x [M]; wt int8 K-blocked [C/64][3C][64] (launch_pack_k64 of W transposed, [3C, C]) with per-column
@@ -64,14 +68,15 @@ int qkv_gemm_k_parts(int C);
 // C must be a multiple of 64.  k_ssq as for launch_qkv_gemm.
 hipError_t launch_qkv_gemm_i8(const int8_t* xq, const int8_t* wt, const float* s_x, const float* s_w, uint16_t* qkv,
                               int64_t M, int C, hipStream_t stream, float* k_ssq = nullptr);
-// Plain bf16 GEMM y[M, NO] = x[M, K] @ w[K, NO] on the same kernel (K a multiple of 32, NO of 8).
-hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t M, int K, int NO,
+// Plain bf16 GEMM y[M, NO] = x[M, K] @ w[K, NO] on the same kernel (K a multiple of 32, NO of 8); xb is
+// x K-blocked, [K/32][M][32].
+hipError_t launch_gemm_bf16(const uint16_t* xb, const uint16_t* w, uint16_t* y, int64_t M, int K, int NO,
                             hipStream_t stream, const char* label = "gemm");
 // Mix-FFN: y = GLU(dwconv3x3(x @ W1)) @ W2 over B grids of Hg x Wg tokens (C channels, width F).  ws
-// holds mix_ffn_workspace_bytes(B*Hg*Wg, F) bytes.  C and F multiples of 32, Wg <= mix_ffn_max_width().
+// holds mix_ffn_workspace_bytes(B*Hg*Wg, C, F) bytes.  C and F multiples of 32, Wg <= mix_ffn_max_width().
 hipError_t launch_mix_ffn(const uint16_t* x, const uint16_t* w1, const uint16_t* kdw, const uint16_t* w2, int B, int Hg,
                           int Wg, int C, int F, uint16_t* out, void* ws, hipStream_t stream);
-size_t mix_ffn_workspace_bytes(int64_t M, int F);
+size_t mix_ffn_workspace_bytes(int64_t M, int C, int F);
 int mix_ffn_max_width();
 // int8 [rows, C] row-major -> K-blocked [C/64][rows][64] (C a multiple of 64).
 hipError_t launch_pack_k64(const int8_t* src, int64_t rows, int C, int8_t* dst, hipStream_t stream);

@@ -6,6 +6,10 @@
 // 8-bit weights and activations while keeping the linear attention in full precision.
 //
 // Block tile 256 (rows of x) x 192 (columns of W), K step 32, 4 waves as 2 x 2, wave tile 128 x 96.
+// x arrives K-blocked, [K/32][M][32] (relayout_k32_kernel writes it from row-major x; the Mix-FFN's
+// conv kernel writes its output so directly): the 16 rows x 64 bytes that one global->LDS instruction
+// stages are then one contiguous 1 KB run instead of 16 pieces of rows 2K bytes apart, which both
+// moves tiles faster and keeps the MFMA issue stream from stalling behind the loads.
 // Tiles of x and W go from global memory straight to LDS (global_load_lds_dwordx4) through a ring of
 // 4 stage buffers, so up to three K steps are in flight while one is multiplied; the buffers are
 // separate LDS objects read through a restrict-qualified pointer, which lets the compiler see that
@@ -118,6 +122,23 @@ __device__ __forceinline__ void read_ops(const char* __restrict__ As, Roles ro, 
   }
 }
 
+// Instruction schedule of one K step: after each of its first NV MFMAs the wave issues one
+// global->LDS load (7 per step), then after each following MFMA three LDS operand reads while any
+// remain (14 or 20 per step), so the MFMA pipe is never left idle while the wave issues memory
+// instructions.  The loads come first: a global->LDS load is a write to LDS, and the compiler makes it
+// wait for every LDS read still outstanding, which after this step's reads would stall the wave.
+template <int I, int NDS, int NV>
+__device__ __forceinline__ void interleave_step() {
+  if constexpr (I < 24) {
+    constexpr int kDsPer = 3;
+    constexpr int ds0 = NDS - (I - NV) * kDsPer, ds = I < NV || ds0 < 0 ? 0 : (ds0 > kDsPer ? kDsPer : ds0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    if constexpr (I < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global->LDS load
+    if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);  // LDS reads
+    interleave_step<I + 1, NDS, NV>();
+  }
+}
+
 template <typename Acc>
 __device__ __forceinline__ void mma(const Ops& op, int s, Acc (&acc)[3][4]) {
 #pragma unroll
@@ -133,8 +154,8 @@ __device__ __forceinline__ void mma(const Ops& op, int s, Acc (&acc)[3][4]) {
 }
 }  // namespace
 
-// x: bf16 [M, K] (I8: int8, K-blocked: [K/64][M][64]); w: bf16 [K, NO] (I8: int8 Wt, K-blocked:
-// [K/64][NO][64]); s_x [M] and s_w [NO]: I8 only.
+// x: K-blocked, [K/32][M][32] bf16 (I8: [K/64][M][64] int8), 64 bytes per row and K step; w: bf16 [K, NO]
+// row-major (I8: int8 Wt, K-blocked: [K/64][NO][64]); s_x [M] and s_w [NO]: I8 only.
 template <bool I8>
 __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const void* __restrict__ x, const void* __restrict__ w,
                                                             const float* __restrict__ s_x,
@@ -161,49 +182,48 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const void* __restri
   if (mb >= mblocks || nb >= nblocks) return;
   const int m0 = mb * BM, n0 = nb * BN;
 
-  // Per-lane sources of this wave's DMA instructions (the K step is added per stage).  A instruction
-  // i covers rows 16i..16i+15 of the x image, B instruction i bytes [1024i, 1024i + 1024) of the W
-  // image (I8: rows 16i..16i+15 of the Wt image, placed like x; both operands K-blocked, so each
-  // instruction reads one contiguous 1 KB run).  Rows past M and columns past NO read
-  // clamped addresses; their products are never stored.
-  const char* a_src[A_DMA];
-  const char* b_src[B_DMA];
+  // Sources of this wave's DMA instructions: a scalar base per K step (block origin + step) plus a
+  // per-lane 32-bit offset fixed for the whole loop, so a step spends one vector add per load on
+  // addresses.  A instruction i covers rows 16i..16i+15 of the x image, B instruction i bytes
+  // [1024i, 1024i + 1024) of the W image (I8: rows 16i..16i+15 of the Wt image, placed like x).  Rows
+  // past M and columns past NO read clamped addresses; their products are never stored.
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // wave index in an SGPR (LDS destinations)
+  uint32_t a_off[A_DMA], b_off[B_DMA];
 #pragma unroll
   for (int a = 0; a < A_DMA; ++a) {
     const int r = 16 * (wave * A_DMA + a) + (lane >> 2);
     const int kc = (lane & 3) ^ xswz(r);
-    // I8: x arrives K-blocked (64-byte slabs, slab t holding row m at byte (t*M + m)*64), so the 16 rows
-    // of one instruction are one contiguous 1 KB run.
-    a_src[a] = I8 ? xb + (int64_t)min(m0 + r, M - 1) * A_ROW + 16 * kc
-                  : xb + (int64_t)min(m0 + r, M - 1) * K * kElem + 16 * kc;
+    // x arrives K-blocked (64-byte slabs, slab t holding row m at byte (t*M + m)*64), so the 16 rows of
+    // one instruction are one contiguous 1 KB run.
+    a_off[a] = (uint32_t)(min(m0 + r, M - 1) - m0) * A_ROW + 16u * kc;
   }
 #pragma unroll
   for (int b = 0; b < B_DMA; ++b) {
     if (I8) {
       const int r = 16 * (wave * B_DMA + b) + (lane >> 2);
       const int kc = (lane & 3) ^ xswz(r);
-      b_src[b] = wbp + (int64_t)min(n0 + r, NO - 1) * A_ROW + 16 * kc;
+      b_off[b] = (uint32_t)(min(n0 + r, NO - 1) - n0) * A_ROW + 16u * kc;
     } else {
       const int off = 1024 * (wave * B_DMA + b) + 16 * lane;
       const int k = off / B_ROW, c = (off % B_ROW) / 16;
       const int nc = c ^ (2 * (k & 3));
-      b_src[b] = wbp + ((int64_t)k * NO + min(n0 + 8 * nc, NO - 8)) * 2;
+      b_off[b] = ((uint32_t)k * NO + (uint32_t)(min(n0 + 8 * nc, NO - 8) - n0)) * 2u;
     }
   }
   const int KT = K * kElem / A_ROW;
   // Every step issues the same 7 instructions per wave (past the last K step they re-read it into a
   // buffer that is not read again), so the number of outstanding loads is the same at every wait.
   auto issue = [&](char* base, int t) {
-    const int tt = min(t, KT - 1);
+    const int64_t tt = min(t, KT - 1);
+    const char* const a_base = xb + (tt * M + m0) * A_ROW;
+    const char* const b_base = I8 ? wbp + (tt * NO + n0) * A_ROW : wbp + (tt * BK * NO + n0) * 2;
 #pragma unroll
     for (int a = 0; a < A_DMA; ++a)
-      __builtin_amdgcn_global_load_lds(a_src[a] + (I8 ? (int64_t)tt * M * A_ROW : (int64_t)tt * A_ROW),
-                                       (lds_ptr_t)(base + 1024 * (wave * A_DMA + a)), 16, 0,
-                                       0);
+      __builtin_amdgcn_global_load_lds(a_base + a_off[a], (lds_ptr_t)(base + 1024 * (wave_s * A_DMA + a)), 16, 0, 0);
 #pragma unroll
     for (int b = 0; b < B_DMA; ++b)
-      __builtin_amdgcn_global_load_lds(b_src[b] + (I8 ? (int64_t)tt * NO * A_ROW : (int64_t)tt * BK * NO * 2),
-                                       (lds_ptr_t)(base + A_BYTES + 1024 * (wave * B_DMA + b)), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(b_base + b_off[b], (lds_ptr_t)(base + A_BYTES + 1024 * (wave_s * B_DMA + b)), 16,
+                                       0, 0);
   };
 
   Acc acc[3][4];
@@ -217,20 +237,23 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const void* __restri
   const Roles ro{128 * wm + (lane & 31), lane >> 5, 96 * wn + 16 * ((lane >> 4) & 1) + 4 * (lane & 3),
                  8 * (lane >> 5) + ((lane >> 2) & 3), 96 * wn + (lane & 31)};
 
-  // Step t (t % STAGES == S) multiplies operands read during step t - 1.  Between its two sub-steps it
-  // waits until stage t + 1 has landed in every wave (stage t + 2 may still be in flight), refills the
-  // buffer of stage t - 1 (its operands were read two steps ago) with stage t + 3, and reads stage
-  // t + 1's operands into the other register set, so their latency overlaps the second sub-step.
+  // Step t (t % STAGES == S) multiplies operands read during step t - 1.  It first waits until stage
+  // t + 1 has landed in every wave (stage t + 2 may still be in flight; the MFMAs of step t - 1 are still
+  // executing), then, interleaved with its 24 MFMAs, refills the buffer of stage t - 1 (its operands
+  // were read two steps ago) with stage t + 3 and reads stage t + 1's operands into the other register
+  // set.
   auto step = [&](auto S_const, int t, Ops& cur, Ops& nxt) {
     constexpr int S = decltype(S_const)::value;
-    mma(cur, 0, acc);
-    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this step's operands, read during the last step
     wait_vm<DMA_PER_STAGE>();
     __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     issue(stage_buf<(S + STAGES - 1) % STAGES>(), t + STAGES - 1);
     read_ops<I8>(stage_buf<(S + 1) % STAGES>(), ro, nxt);
-    __builtin_amdgcn_sched_barrier(0);
+    mma(cur, 0, acc);
     mma(cur, 1, acc);
+    interleave_step<0, I8 ? 14 : 20, DMA_PER_STAGE>();
+    __builtin_amdgcn_sched_barrier(0);
   };
   const std::integral_constant<int, 0> S0{};
   const std::integral_constant<int, 1> S1{};
@@ -313,6 +336,9 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const void* __restri
   }
 }
 
+// The per-lane DMA offsets are 32-bit: at most 255 rows x K x 2 bytes (x) and 32 x NO x 2 bytes (W).
+constexpr int kMaxK = 1 << 20, kMaxNO = 1 << 24;
+
 int qkv_gemm_k_parts(int C) { return (2 * C - 1) / BN - C / BN + 1; }
 
 // Per-row symmetric int8 quantisation of bf16 x [M, C] (the dynamic activation half of W8A8): with
@@ -390,6 +416,32 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int C, int8_t* xq, fl
   return hipGetLastError();
 }
 
+// x [M][K] bf16 row-major -> xb [K/32][M][32] (the GEMM's x layout; K a multiple of 32).  Wave w of
+// block (bx, by) moves rows 64 bx + 16 w + l/4 (lane l) of the 32-column groups [8 by, 8 by + 8): the
+// 16-byte unit l % 4 of each group.  Its eight loads are issued before its stores, and each store
+// instruction writes one contiguous 1 KB run (16 rows x 64 bytes).
+__global__ __launch_bounds__(256) void relayout_k32_kernel(const uint16_t* __restrict__ x, int64_t M, int K,
+                                                           uint16_t* __restrict__ xb) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t m = (int64_t)blockIdx.x * 64 + 16 * wave + (lane >> 2);
+  const int G = K / 32, g0 = (int)blockIdx.y * 8;
+  if (m >= M) return;
+  u32x4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (g0 + i < G) v[i] = load16(x + m * K + (g0 + i) * 32 + 8 * (lane & 3));
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (g0 + i < G) store16(xb + ((int64_t)(g0 + i) * M + m) * 32 + 8 * (lane & 3), v[i]);
+}
+
+hipError_t launch_relayout_k32(const uint16_t* x, int64_t M, int K, uint16_t* xb, hipStream_t stream) {
+  if (K % 32 != 0 || M > (1LL << 30) || K / 256 >= 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((M + 63) / 64), (unsigned)((K / 32 + 7) / 8));
+  SANA_LAUNCH("relayout_x", relayout_k32_kernel<<<grid, 256, 0, stream>>>(x, M, K, xb));
+  return hipGetLastError();
+}
+
 // One thread per 16-byte unit u of row n: src[n][16u..16u+15] -> dst[u/4][n][16(u%4)..].
 __global__ __launch_bounds__(256) void pack_k64_kernel(const int8_t* __restrict__ src, int64_t rows, int C,
                                                        int8_t* __restrict__ dst) {
@@ -409,34 +461,34 @@ hipError_t launch_pack_k64(const int8_t* src, int64_t rows, int C, int8_t* dst, 
   return hipGetLastError();
 }
 
-hipError_t launch_qkv_gemm(const uint16_t* x, const uint16_t* w, uint16_t* qkv, int64_t M, int C, hipStream_t stream,
-                           float* k_ssq) {
+hipError_t launch_qkv_gemm(const uint16_t* xb, const uint16_t* w, uint16_t* qkv, int64_t M, int C,
+                           hipStream_t stream, float* k_ssq) {
   const int NO = 3 * C;
-  if (C % BK != 0 || M > (1LL << 30)) return hipErrorInvalidValue;
+  if (C % BK != 0 || M > (1LL << 30) || C > kMaxK) return hipErrorInvalidValue;
   const int mblocks = (int)((M + BM - 1) / BM), nblocks = (NO + BN - 1) / BN;
   const int slab = mblocks >= 8 ? (mblocks + 7) / 8 : 0;
   const int64_t blocks = slab > 0 ? (int64_t)8 * slab * nblocks : (int64_t)mblocks * nblocks;
   SANA_LAUNCH("qkv_gemm", qkv_gemm_kernel<false><<<(unsigned)blocks, kThreads, 0, stream>>>(
-                              x, w, nullptr, nullptr, qkv, (int)M, C, NO, mblocks, nblocks, slab, k_ssq,
+                              xb, w, nullptr, nullptr, qkv, (int)M, C, NO, mblocks, nblocks, slab, k_ssq,
                               qkv_gemm_k_parts(C)));
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t M, int K, int NO,
+hipError_t launch_gemm_bf16(const uint16_t* xb, const uint16_t* w, uint16_t* y, int64_t M, int K, int NO,
                             hipStream_t stream, const char* label) {
-  if (K % BK != 0 || NO % 8 != 0 || M > (1LL << 30)) return hipErrorInvalidValue;
+  if (K % BK != 0 || NO % 8 != 0 || M > (1LL << 30) || K > kMaxK || NO > kMaxNO) return hipErrorInvalidValue;
   const int mblocks = (int)((M + BM - 1) / BM), nblocks = (NO + BN - 1) / BN;
   const int slab = mblocks >= 8 ? (mblocks + 7) / 8 : 0;
   const int64_t blocks = slab > 0 ? (int64_t)8 * slab * nblocks : (int64_t)mblocks * nblocks;
   SANA_LAUNCH(label, qkv_gemm_kernel<false><<<(unsigned)blocks, kThreads, 0, stream>>>(
-                          x, w, nullptr, nullptr, y, (int)M, K, NO, mblocks, nblocks, slab, nullptr, 0));
+                          xb, w, nullptr, nullptr, y, (int)M, K, NO, mblocks, nblocks, slab, nullptr, 0));
   return hipGetLastError();
 }
 
 hipError_t launch_qkv_gemm_i8(const int8_t* xq, const int8_t* wt, const float* s_x, const float* s_w, uint16_t* qkv,
                               int64_t M, int C, hipStream_t stream, float* k_ssq) {
   const int NO = 3 * C;
-  if (C % (2 * BK) != 0 || M > (1LL << 30)) return hipErrorInvalidValue;
+  if (C % (2 * BK) != 0 || M > (1LL << 30) || C > kMaxK) return hipErrorInvalidValue;
   const int mblocks = (int)((M + BM - 1) / BM), nblocks = (NO + BN - 1) / BN;
   const int slab = mblocks >= 8 ? (mblocks + 7) / 8 : 0;
   const int64_t blocks = slab > 0 ? (int64_t)8 * slab * nblocks : (int64_t)mblocks * nblocks;

@@ -27,7 +27,7 @@ constexpr int kThreads = 256;
 int mix_ffn_max_width() { return 128; }
 
 // h: [B, Hg*Wg, 2F] bf16 (values | gates); kdw: [2F][9] bf16 (tap 3p + q reads row i+p-1, column
-// j+q-1); g: [B, Hg*Wg, F] bf16.  F is a multiple of 8; Wg <= 16 * UNITS.  Row loads are range-checked
+// j+q-1); g: bf16, K-blocked for the projection, [F/32][B*Hg*Wg][32] (gridDim.y = B).  F is a multiple of 8; Wg <= 16 * UNITS.  Row loads are range-checked
 // buffer loads (rows past Hg and channels past F read zeros without traffic), two rows ahead of the
 // row being formed, in two register sets.
 template <int UNITS>
@@ -122,7 +122,9 @@ __global__ __launch_bounds__(kThreads, 2) void dwconv_glu_kernel(const uint16_t*
           float gv[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) gv[e] = a[k][e] * __builtin_amdgcn_rcpf(1.f + __expf(-z[k][e]));
-          *reinterpret_cast<uint2*>(g + ((int64_t)b * N + (int64_t)i * Wg + j0 + k) * F + cv) =
+          // g is stored K-blocked for the projection GEMM: [F/32][M][32], M = B * N.
+          const int64_t m = (int64_t)b * N + (int64_t)i * Wg + j0 + k;
+          *reinterpret_cast<uint2*>(g + (((int64_t)(cv >> 5) * gridDim.y * N + m) << 5) + (cv & 31)) =
               make_uint2(cvt_pk_bf16(gv[0], gv[1]), cvt_pk_bf16(gv[2], gv[3]));
         }
       }
@@ -160,8 +162,11 @@ hipError_t launch_mix_ffn(const uint16_t* x, const uint16_t* w1, const uint16_t*
                           int Wg, int C, int F, uint16_t* out, void* ws, hipStream_t stream) {
   const int64_t M = (int64_t)B * Hg * Wg;
   uint16_t* hbuf = static_cast<uint16_t*>(ws);
+  // The second region holds x K-blocked for the expansion GEMM, then g (K-blocked) for the projection.
   uint16_t* gbuf = hbuf + (M * 2 * F + 127) / 128 * 128;
-  hipError_t e = launch_gemm_bf16(x, w1, hbuf, M, C, 2 * F, stream, "gemm_expand");
+  hipError_t e = launch_relayout_k32(x, M, C, gbuf, stream);
+  if (e != hipSuccess) return e;
+  e = launch_gemm_bf16(gbuf, w1, hbuf, M, C, 2 * F, stream, "gemm_expand");
   if (e != hipSuccess) return e;
   const size_t lds = (size_t)3 * ((Wg + 3) / 4 * 4 + 2) * kTokBytes;
   static bool attr_set = false;
@@ -190,8 +195,8 @@ hipError_t launch_mix_ffn(const uint16_t* x, const uint16_t* w1, const uint16_t*
   return launch_gemm_bf16(gbuf, w2, out, M, F, C, stream, "gemm_project");
 }
 
-size_t mix_ffn_workspace_bytes(int64_t M, int F) {
-  return (size_t)((M * 2 * F + 127) / 128 * 128) * 2 + (size_t)M * F * 2;
+size_t mix_ffn_workspace_bytes(int64_t M, int C, int F) {
+  return (size_t)((M * 2 * F + 127) / 128 * 128) * 2 + (size_t)M * std::max(C, F) * 2;
 }
 
 }  // namespace sanala

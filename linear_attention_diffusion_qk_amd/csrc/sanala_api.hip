@@ -238,16 +238,24 @@ extern "C" sana_status_t sana_qkv_linear_attn_fwd(const void* x, const void* Wqk
   const size_t qkv_bytes = ((size_t)M * 3 * C * 2 + 255) / 256 * 256;
   const int k_parts = norm ? sanala::qkv_gemm_k_parts((int)C) : 0;
   const size_t ssq_bytes = ((size_t)M * k_parts * 4 + 255) / 256 * 256;
+  const size_t xb_bytes = ((size_t)M * C * 2 + 255) / 256 * 256;  // x K-blocked for the GEMM
   ScratchLease lease;
-  if (lease.acquire(dev, stream, qkv_bytes + ssq_bytes + plan.ws_bytes) != hipSuccess) return SANA_ERR_HIP;
-  void* ws = lease.ptr();
-  uint16_t* qkv = static_cast<uint16_t*>(ws);
-  float* k_ssq = norm ? reinterpret_cast<float*>(static_cast<char*>(ws) + qkv_bytes) : nullptr;
-  hipError_t e = sanala::launch_qkv_gemm(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(Wqkv), qkv, M,
-                                         (int)C, stream, k_ssq);
+  if (lease.acquire(dev, stream, qkv_bytes + ssq_bytes + std::max(xb_bytes, plan.ws_bytes)) != hipSuccess)
+    return SANA_ERR_HIP;
+  char* ws = static_cast<char*>(lease.ptr());
+  uint16_t* qkv = reinterpret_cast<uint16_t*>(ws);
+  float* k_ssq = norm ? reinterpret_cast<float*>(ws + qkv_bytes) : nullptr;
+  // The blocked copy of x and the attention workspace share a region: the GEMM is done with the first
+  // before the attention kernels use the second (stream order).
+  char* region = ws + qkv_bytes + ssq_bytes;
+  hipError_t e = sanala::launch_relayout_k32(static_cast<const uint16_t*>(x), M, (int)C,
+                                             reinterpret_cast<uint16_t*>(region), stream);
   if (e == hipSuccess)
-    e = sanala::launch_attn(plan, qkv, 3 * C, qkv + C, qkv + 2 * C, 3 * C, gq, gk, eps, out, C,
-                            static_cast<char*>(ws) + qkv_bytes + ssq_bytes, stream, k_ssq, k_parts);
+    e = sanala::launch_qkv_gemm(reinterpret_cast<const uint16_t*>(region), static_cast<const uint16_t*>(Wqkv), qkv, M,
+                                (int)C, stream, k_ssq);
+  if (e == hipSuccess)
+    e = sanala::launch_attn(plan, qkv, 3 * C, qkv + C, qkv + 2 * C, 3 * C, gq, gk, eps, out, C, region, stream, k_ssq,
+                            k_parts);
   return e == hipSuccess ? SANA_OK : SANA_ERR_HIP;
 }
 
@@ -257,6 +265,7 @@ extern "C" sana_status_t sana_mix_ffn_fwd(const void* x, const void* W1, const v
   if (!x || !W1 || !Wdw || !W2 || !out) return SANA_ERR_INVALID_ARG;
   if (B < 1 || Hg < 1 || Wg < 1 || C < 1 || F < 1) return SANA_ERR_INVALID_ARG;
   if (C % 32 != 0 || F % 32 != 0 || Wg > sanala::mix_ffn_max_width() || B > 65535) return SANA_ERR_UNSUPPORTED;
+  if (C > (1 << 20) || F > (1 << 20)) return SANA_ERR_UNSUPPORTED;
   const int64_t M = (int64_t)B * Hg * Wg;
   if (M > (int64_t(1) << 30) || (double)M * 2.0 * F >= 1099511627776.0) return SANA_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(W1) || !aligned16(W2) || !aligned16(out) || (reinterpret_cast<uintptr_t>(Wdw) & 1))
@@ -270,7 +279,7 @@ extern "C" sana_status_t sana_mix_ffn_fwd(const void* x, const void* W1, const v
   init_pool(dev);
   g_timing.count = 0;
   ScratchLease lease;
-  if (lease.acquire(dev, stream, sanala::mix_ffn_workspace_bytes(M, F)) != hipSuccess) return SANA_ERR_HIP;
+  if (lease.acquire(dev, stream, sanala::mix_ffn_workspace_bytes(M, C, F)) != hipSuccess) return SANA_ERR_HIP;
   const hipError_t e = sanala::launch_mix_ffn(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W1),
                                               static_cast<const uint16_t*>(Wdw), static_cast<const uint16_t*>(W2), B,
                                               Hg, Wg, C, F, static_cast<uint16_t*>(out), lease.ptr(), stream);
