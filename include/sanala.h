@@ -90,7 +90,8 @@ sana_status_t sana_linear_attn_fwd(const void* q, const void* k, const void* v,
  *   out      device bf16 [B, N, C]; fully overwritten.
  *   stream   HIP stream.
  *
- * The qkv intermediate (B*N*3C bf16) lives in the stream's scratch.  Errors as above.
+ * The qkv intermediate (B*N*3C bf16) and a copy of x laid out for the projection GEMM live in the
+ * stream's scratch.  Errors as above.
  */
 sana_status_t sana_qkv_linear_attn_fwd(const void* x, const void* Wqkv,
                                        const float* gq, const float* gk,
@@ -149,7 +150,8 @@ sana_status_t sana_qkv_w8a8_linear_attn_fwd(const void* x, const void* Wt_p, con
  *   B, Hg, Wg  >= 1, Wg <= 128; C and F multiples of 32, at most 2^20 (SANA: C = 2240, F = 5600).
  *   out      device bf16 [B, Hg*Wg, C], 16-byte aligned, not overlapping the inputs; fully overwritten.
  *
- * Scratch (the stream's buffer): h (B*Hg*Wg*2F bf16) and g (B*Hg*Wg*F bf16).  Errors as above.
+ * Scratch (the stream's buffer): h (B*Hg*Wg*2F bf16) and B*Hg*Wg*max(C, F) bf16 for a copy of x laid out
+ * for the expansion GEMM, later reused for g.  Errors as above.
  */
 sana_status_t sana_mix_ffn_fwd(const void* x, const void* W1, const void* Wdw, const void* W2,
                                int B, int Hg, int Wg, int C, int F, void* out, hipStream_t stream);
