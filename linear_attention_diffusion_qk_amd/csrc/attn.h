@@ -69,9 +69,10 @@ int qkv_gemm_k_parts(int C);
 hipError_t launch_qkv_gemm_i8(const int8_t* xq, const int8_t* wt, const float* s_x, const float* s_w, uint16_t* qkv,
                               int64_t M, int C, hipStream_t stream, float* k_ssq = nullptr);
 // Plain bf16 GEMM y[M, NO] = x[M, K] @ w[K, NO] on the same kernel (K a multiple of 32, NO of 8); xb is
-// x K-blocked, [K/32][M][32].
+// x K-blocked, [K/32][M][32]; with y_blocked, y is stored the same way, [NO/32][M][32] (NO a multiple
+// of 32).
 hipError_t launch_gemm_bf16(const uint16_t* xb, const uint16_t* w, uint16_t* y, int64_t M, int K, int NO,
-                            hipStream_t stream, const char* label = "gemm");
+                            hipStream_t stream, const char* label = "gemm", bool y_blocked = false);
 // Mix-FFN: y = GLU(dwconv3x3(x @ W1)) @ W2 over B grids of Hg x Wg tokens (C channels, width F).  ws
 // holds mix_ffn_workspace_bytes(B*Hg*Wg, C, F) bytes.  C and F multiples of 32, Wg <= mix_ffn_max_width().
 hipError_t launch_mix_ffn(const uint16_t* x, const uint16_t* w1, const uint16_t* kdw, const uint16_t* w2, int B, int Hg,

@@ -155,8 +155,9 @@ __device__ __forceinline__ void mma(const Ops& op, int s, Acc (&acc)[3][4]) {
 }  // namespace
 
 // x: K-blocked, [K/32][M][32] bf16 (I8: [K/64][M][64] int8), 64 bytes per row and K step; w: bf16 [K, NO]
-// row-major (I8: int8 Wt, K-blocked: [K/64][NO][64]); s_x [M] and s_w [NO]: I8 only.
-template <bool I8>
+// row-major (I8: int8 Wt, K-blocked: [K/64][NO][64]); s_x [M] and s_w [NO]: I8 only.  y: [M][NO]
+// row-major, or with Y_BLK [NO/32][M][32] (NO a multiple of 32), the layout the Mix-FFN's conv reads.
+template <bool I8, bool Y_BLK>
 __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const void* __restrict__ x, const void* __restrict__ w,
                                                             const float* __restrict__ s_x,
                                                             const float* __restrict__ s_w,
@@ -314,7 +315,9 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const void* __restri
         const uint32_t p0 = cvt_pk_bf16(v4[0], v4[1]);
         const uint32_t p1 = cvt_pk_bf16(v4[2], v4[3]);
         if (n < NO) {
-          uint32_t* dst = reinterpret_cast<uint32_t*>(y + (int64_t)m * NO + n);
+          // n % 4 == 0, so the 4 columns stay inside one 32-column chunk of the blocked layout.
+          uint32_t* dst = reinterpret_cast<uint32_t*>(
+              Y_BLK ? y + (((int64_t)(n >> 5) * M + m) << 5) + (n & 31) : y + (int64_t)m * NO + n);
           dst[0] = p0;
           dst[1] = p1;
         }
@@ -468,20 +471,25 @@ hipError_t launch_qkv_gemm(const uint16_t* xb, const uint16_t* w, uint16_t* qkv,
   const int mblocks = (int)((M + BM - 1) / BM), nblocks = (NO + BN - 1) / BN;
   const int slab = mblocks >= 8 ? (mblocks + 7) / 8 : 0;
   const int64_t blocks = slab > 0 ? (int64_t)8 * slab * nblocks : (int64_t)mblocks * nblocks;
-  SANA_LAUNCH("qkv_gemm", qkv_gemm_kernel<false><<<(unsigned)blocks, kThreads, 0, stream>>>(
+  SANA_LAUNCH("qkv_gemm", qkv_gemm_kernel<false, false><<<(unsigned)blocks, kThreads, 0, stream>>>(
                               xb, w, nullptr, nullptr, qkv, (int)M, C, NO, mblocks, nblocks, slab, k_ssq,
                               qkv_gemm_k_parts(C)));
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16(const uint16_t* xb, const uint16_t* w, uint16_t* y, int64_t M, int K, int NO,
-                            hipStream_t stream, const char* label) {
+                            hipStream_t stream, const char* label, bool y_blocked) {
   if (K % BK != 0 || NO % 8 != 0 || M > (1LL << 30) || K > kMaxK || NO > kMaxNO) return hipErrorInvalidValue;
+  if (y_blocked && NO % 32 != 0) return hipErrorInvalidValue;
   const int mblocks = (int)((M + BM - 1) / BM), nblocks = (NO + BN - 1) / BN;
   const int slab = mblocks >= 8 ? (mblocks + 7) / 8 : 0;
   const int64_t blocks = slab > 0 ? (int64_t)8 * slab * nblocks : (int64_t)mblocks * nblocks;
-  SANA_LAUNCH(label, qkv_gemm_kernel<false><<<(unsigned)blocks, kThreads, 0, stream>>>(
-                          xb, w, nullptr, nullptr, y, (int)M, K, NO, mblocks, nblocks, slab, nullptr, 0));
+  if (y_blocked)
+    SANA_LAUNCH(label, qkv_gemm_kernel<false, true><<<(unsigned)blocks, kThreads, 0, stream>>>(
+                            xb, w, nullptr, nullptr, y, (int)M, K, NO, mblocks, nblocks, slab, nullptr, 0));
+  else
+    SANA_LAUNCH(label, qkv_gemm_kernel<false, false><<<(unsigned)blocks, kThreads, 0, stream>>>(
+                            xb, w, nullptr, nullptr, y, (int)M, K, NO, mblocks, nblocks, slab, nullptr, 0));
   return hipGetLastError();
 }
 
@@ -492,7 +500,7 @@ hipError_t launch_qkv_gemm_i8(const int8_t* xq, const int8_t* wt, const float* s
   const int mblocks = (int)((M + BM - 1) / BM), nblocks = (NO + BN - 1) / BN;
   const int slab = mblocks >= 8 ? (mblocks + 7) / 8 : 0;
   const int64_t blocks = slab > 0 ? (int64_t)8 * slab * nblocks : (int64_t)mblocks * nblocks;
-  SANA_LAUNCH("qkv_gemm_i8", qkv_gemm_kernel<true><<<(unsigned)blocks, kThreads, 0, stream>>>(
+  SANA_LAUNCH("qkv_gemm_i8", qkv_gemm_kernel<true, false><<<(unsigned)blocks, kThreads, 0, stream>>>(
                                  xq, wt, s_x, s_w, qkv, (int)M, C, NO, mblocks, nblocks, slab, k_ssq,
                                  qkv_gemm_k_parts(C)));
   return hipGetLastError();

@@ -26,10 +26,12 @@ constexpr int kThreads = 256;
 
 int mix_ffn_max_width() { return 128; }
 
-// h: [B, Hg*Wg, 2F] bf16 (values | gates); kdw: [2F][9] bf16 (tap 3p + q reads row i+p-1, column
-// j+q-1); g: bf16, K-blocked for the projection, [F/32][B*Hg*Wg][32] (gridDim.y = B).  F is a multiple of 8; Wg <= 16 * UNITS.  Row loads are range-checked
-// buffer loads (rows past Hg and channels past F read zeros without traffic), two rows ahead of the
-// row being formed, in two register sets.
+// h: bf16, chunk-major [2F/32][M][32] (channel c of token m at ((c / 32) * M + m) * 32 + c % 32, M =
+// B*Hg*Wg; values are channels [0, F), gates [F, 2F)), as the expansion GEMM stores it; kdw: [2F][9] bf16
+// (tap 3p + q reads row i+p-1, column j+q-1); g: bf16, K-blocked for the projection, [F/32][M][32].
+// gridDim.y = B.  F is a multiple of 32; Wg <= 16 * UNITS.  Row loads are masked (rows past Hg and
+// channels past F read zeros without memory traffic), two rows ahead of the row being formed, in two
+// register sets.
 template <int UNITS>
 __global__ __launch_bounds__(kThreads, 2) void dwconv_glu_kernel(const uint16_t* __restrict__ h,
                                                                  const uint16_t* __restrict__ kdw,
@@ -40,9 +42,8 @@ __global__ __launch_bounds__(kThreads, 2) void dwconv_glu_kernel(const uint16_t*
   const int r0 = blockIdx.z * rows_per_block, r1 = min(Hg, r0 + rows_per_block);  // output rows of the block
   const int c0 = chunk * kCh;
   const int N = Hg * Wg;
-  const int64_t ld = 2 * (int64_t)F;
+  const int64_t Mtot = (int64_t)gridDim.y * N;
   const int slot_bytes = ((Wg + 3) / 4 * 4 + 2) * kTokBytes;  // halo column, Wg rounded up to 4, halo
-  const __amdgpu_buffer_rsrc_t hr = make_rsrc(h + (int64_t)b * N * ld, (uint32_t)((int64_t)N * ld * 2));
 
   // This lane's channel group (4 value channels c0 + 4cg.., the gates F + the same) and its taps.
   const int cg = tid & 15;
@@ -57,24 +58,35 @@ __global__ __launch_bounds__(kThreads, 2) void dwconv_glu_kernel(const uint16_t*
       wb[e][t] = cvalid ? __uint_as_float((uint32_t)kdw[(int64_t)(F + cv + e) * 9 + t] << 16) : 0.f;
     }
 
-  // Unit u of a row = token u / 16, part u % 16 (0..7 value units, 8..15 gate units).
+  // Unit u of a row: chunk q = u / (4 Wg) (q = 0, 1: value channels c0 + 32q ..; q = 2, 3: the gates
+  // F + c0 + 32(q - 2) ..), token t = (u / 4) % Wg, 16-byte piece w = u % 4; so one wave's load covers 16
+  // tokens of one chunk, 1 KB of consecutive bytes.  In LDS the unit goes to token t, part 4q + w
+  // (0..7 values, 8..15 gates).  The roles do not depend on the row: the row adds i * Wg * 64 bytes.
   const int units = Wg * 16;
-  auto load_row = [&](int i, u32x4 (&pre)[UNITS]) {
+  const uint16_t* src[UNITS];
+  int lds_off[UNITS];
+  bool uok[UNITS];
 #pragma unroll
-    for (int k = 0; k < UNITS; ++k) {
-      const int u = tid + k * kThreads;
-      const int tok = u >> 4, part = u & 15, cc = c0 + 8 * (part & 7);
-      const bool ok = u < units && i >= 0 && i < Hg && cc < F;
-      const int64_t off = (((int64_t)i * Wg + tok) * ld + (part < 8 ? 0 : F) + cc) * 2;
-      pre[k] = buffer_load16(hr, ok ? (uint32_t)off : kOutOfRange);
-    }
+  for (int k = 0; k < UNITS; ++k) {
+    const int u = tid + k * kThreads;
+    const int q = u / (4 * Wg), rem = u - q * 4 * Wg, t = rem >> 2, w = rem & 3;
+    const int ch = ((q < 2 ? c0 : F + c0) >> 5) + (q & 1);  // F and c0 are multiples of 32
+    uok[k] = u < units && c0 + 32 * (q & 1) + 8 * w < F;
+    src[k] = h + (((int64_t)ch * Mtot + (int64_t)b * N + t) << 5) + 8 * w;
+    lds_off[k] = (t + 1) * kTokBytes + (4 * q + w) * 16;
+  }
+  auto load_row = [&](int i, u32x4 (&pre)[UNITS]) {
+    const bool row_ok = i >= 0 && i < Hg;
+#pragma unroll
+    for (int k = 0; k < UNITS; ++k)
+      pre[k] = row_ok && uok[k] ? load16(src[k] + ((int64_t)i * Wg << 5)) : u32x4{0u, 0u, 0u, 0u};
   };
   auto store_row = [&](int slot, const u32x4 (&pre)[UNITS]) {
     char* base = ring + slot * slot_bytes;
 #pragma unroll
     for (int k = 0; k < UNITS; ++k) {
       const int u = tid + k * kThreads;
-      if (u < units) store16(base + ((u >> 4) + 1) * kTokBytes + (u & 15) * 16, pre[k]);
+      if (u < units) store16(base + lds_off[k], pre[k]);
     }
   };
   auto slot_of = [&](int i) { return (i - r0 + 1) % 3; };  // i >= r0 - 1
@@ -166,7 +178,7 @@ hipError_t launch_mix_ffn(const uint16_t* x, const uint16_t* w1, const uint16_t*
   uint16_t* gbuf = hbuf + (M * 2 * F + 127) / 128 * 128;
   hipError_t e = launch_relayout_k32(x, M, C, gbuf, stream);
   if (e != hipSuccess) return e;
-  e = launch_gemm_bf16(gbuf, w1, hbuf, M, C, 2 * F, stream, "gemm_expand");
+  e = launch_gemm_bf16(gbuf, w1, hbuf, M, C, 2 * F, stream, "gemm_expand", true);
   if (e != hipSuccess) return e;
   const size_t lds = (size_t)3 * ((Wg + 3) / 4 * 4 + 2) * kTokBytes;
   static bool attr_set = false;
