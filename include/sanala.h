@@ -45,7 +45,7 @@ extern "C" {
 typedef enum {
   SANA_OK = 0,
   SANA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad eps, only one gain NULL, ... */
-  SANA_ERR_UNSUPPORTED = 2, /* a shape or dtype this build has no kernel for (D != 32, ...) */
+  SANA_ERR_UNSUPPORTED = 2, /* a shape or dtype the library has no kernel for (D != 32, ...) */
   SANA_ERR_MISALIGNED = 3,  /* a tensor pointer is not 16-byte aligned */
   SANA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
 } sana_status_t;

@@ -15,7 +15,7 @@ Sources (web pages, cited by title and section):
             section "model architecture", bullet "QK Norm": RMSNorm on the
             queries and keys of the linear self-attention.
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
   * RMSNorm spans all C = H*D channels of a token (before the head split),
     has a gain vector over C and no bias or mean subtraction; it is applied
     before ReLU: phi(x) = ReLU(x / sqrt(mean_c x_c^2 + eps) * g).

@@ -12,7 +12,7 @@ Sources (web pages, cited by title and section):
   [SANA1.5] "SANA 1.5: ..." (research notes), model architecture bullet on
             scale: 2240 channels per block and an FFN width of 5600.
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
   * Tokens form an Hg x Wg grid in raster order, token n = i * Wg + j (square
     latents: Hg = Wg = sqrt(N)).
   * The inverted residual block expands with a pointwise (1x1) projection

@@ -8,7 +8,7 @@ model is deployed with INT8 weights and INT8 activations (W8A8), while the
 normalisation layers, the linear attention and the cross-attention KV stay in
 full precision.
 
-Readings where the page names only "W8A8" (each is listed in the design doc):
+Readings where the page names only "W8A8":
   * Symmetric int8 with codes in [-127, 127] and no zero point.
   * Activations are quantised per token (row of x) with a scale taken from the
     row itself at run time; weights per output column, offline.
