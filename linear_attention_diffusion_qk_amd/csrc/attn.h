@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cstddef>
 #include <cstdint>
@@ -89,14 +90,21 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int C, int8_t* xq, fl
 
 // Measurement hooks (no-ops unless timing is enabled on the calling host thread): an event pair is
 // recorded on `s` around each kernel launch.
-void timing_begin(const char* name, hipStream_t s);
-void timing_end(hipStream_t s);
+// Kernel timing (sana_timing_enable): the next pair of events of the calling thread, labelled `name`;
+// false when timing is off.
+bool timing_slot(const char* name, hipEvent_t* begin, hipEvent_t* end);
 
-#define SANA_LAUNCH(name, ...)  \
-  do {                          \
-    timing_begin(name, stream); \
-    __VA_ARGS__;                \
-    timing_end(stream);         \
-  } while (0)
+// kernel<<<grid, block, lds, stream>>>(args...).  With timing on, the launch goes through
+// hipExtLaunchKernelGGL with a start/stop event pair that the dispatch itself timestamps, so the
+// recorded duration is the kernel's own (no event packets between kernels).
+template <typename... P, typename... A>
+inline void launch_kernel(const char* name, void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                          A... args) {
+  hipEvent_t b = nullptr, e = nullptr;
+  if (timing_slot(name, &b, &e))
+    hipExtLaunchKernelGGL(kernel, grid, block, (std::uint32_t)lds, stream, b, e, 0u, args...);
+  else
+    kernel<<<grid, block, lds, stream>>>(args...);
+}
 
 }  // namespace sanala

@@ -582,28 +582,29 @@ static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t l
   float* r_q = reinterpret_cast<float*>(base + p.off_rq);
   const bool groups = p.out_kind == kOutTileGroups;
   if (p.norm && groups)  // r_k and r_q in one launch (the output blocks see only some heads of a row)
-    SANA_LAUNCH("rowstats_kq", rowstats_kernel<uint16_t, F16><<<(unsigned)((2 * rows + 3) / 4), 256, 0, stream>>>(
-                                   k, ldkv, rows, C, eps, r_k, q, ldq, r_q));
+    launch_kernel("rowstats_kq", rowstats_kernel<uint16_t, F16>, (unsigned)((2 * rows + 3) / 4), 256, 0, stream, k,
+                  ldkv, rows, C, eps, r_k, q, ldq, r_q);
   else if (p.norm && k_ssq)
-    SANA_LAUNCH("rowfinish_k", rowfinish_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(
-                                   k_ssq, k_parts, rows, inv_C, eps, r_k));
+    launch_kernel("rowfinish_k", rowfinish_kernel, (unsigned)((rows + 255) / 256), 256, 0, stream, k_ssq, k_parts, rows,
+                  inv_C, eps, r_k);
   else if (p.norm)
-    SANA_LAUNCH("rowstats_k", rowstats_kernel<uint16_t, F16><<<rs_blocks, 256, 0, stream>>>(k, ldkv, rows, C, eps, r_k));
+    launch_kernel("rowstats_k", rowstats_kernel<uint16_t, F16>, rs_blocks, 256, 0, stream, k, ldkv, rows, C, eps, r_k,
+                  nullptr, 0, nullptr);
   const dim3 grid(p.NC, (H + 1) / 2, B);
   if (p.norm)
-    SANA_LAUNCH("kv_state", kv_state_bf16<true, F16><<<grid, 256, 0, stream>>>(k, v, ldkv, r_k, gq, gk, N, H, p.Tc, p.NC,
-                                                                          part, Sop, zop, gsg));
+    launch_kernel("kv_state", kv_state_bf16<true, F16>, grid, 256, 0, stream, k, v, ldkv, r_k, gq, gk, N, H, p.Tc, p.NC,
+                  part, Sop, zop, gsg);
   else
-    SANA_LAUNCH("kv_state", kv_state_bf16<false, F16><<<grid, 256, 0, stream>>>(k, v, ldkv, nullptr, nullptr, nullptr, N, H,
-                                                                           p.Tc, p.NC, part, Sop, zop, gsg));
+    launch_kernel("kv_state", kv_state_bf16<false, F16>, grid, 256, 0, stream, k, v, ldkv, nullptr, nullptr, nullptr, N,
+                  H, p.Tc, p.NC, part, Sop, zop, gsg);
   if (p.NC > 1) {
     const unsigned blocks = (unsigned)((BH * kPartStride + 255) / 256);
     if (p.norm)
-      SANA_LAUNCH("kv_reduce",
-                  kv_reduce_bf16<true><<<blocks, 256, 0, stream>>>(part, p.NC, H, BH, gq, gk, Sop, zop, gsg));
+      launch_kernel("kv_reduce", kv_reduce_bf16<true>, blocks, 256, 0, stream, part, p.NC, H, BH, gq, gk, Sop, zop,
+                    gsg);
     else
-      SANA_LAUNCH("kv_reduce",
-                  kv_reduce_bf16<false><<<blocks, 256, 0, stream>>>(part, p.NC, H, BH, nullptr, nullptr, Sop, zop, gsg));
+      launch_kernel("kv_reduce", kv_reduce_bf16<false>, blocks, 256, 0, stream, part, p.NC, H, BH, nullptr, nullptr,
+                    Sop, zop, gsg);
   }
 
   if (p.out_kind == kOutPersist) {
@@ -623,42 +624,43 @@ static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t l
       attr_set = true;
     }
     if (p.norm)
-      SANA_LAUNCH("out", out_persist_bf16<kPersistPPW, true, F16><<<nblk, nw * 64, lds, stream>>>(
-                             q, ldq, gsg, Sop, zop, B, N, H, eps, inv_C, out, ldo, per_arg));
+      launch_kernel("out", out_persist_bf16<kPersistPPW, true, F16>, nblk, nw * 64, lds, stream, q, ldq, gsg, Sop, zop,
+                    B, N, H, eps, inv_C, out, ldo, per_arg);
     else
-      SANA_LAUNCH("out", out_persist_bf16<kPersistPPW, false, F16><<<nblk, nw * 64, lds, stream>>>(
-                             q, ldq, gsg, Sop, zop, B, N, H, eps, inv_C, out, ldo, per_arg));
+      launch_kernel("out", out_persist_bf16<kPersistPPW, false, F16>, nblk, nw * 64, lds, stream, q, ldq, gsg, Sop, zop,
+                    B, N, H, eps, inv_C, out, ldo, per_arg);
     return hipGetLastError();
   }
   if (groups) {
     constexpr int HPWG = 5;  // 20 heads per block
     const dim3 ogrid((N + 15) / 16, B, (H + 4 * HPWG - 1) / (4 * HPWG));
     if (p.norm)
-      SANA_LAUNCH("out", out_bf16<HPWG, true, true, F16><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, r_q, N, H,
-                                                                                   eps, inv_C, out, ldo));
+      launch_kernel("out", out_bf16<HPWG, true, true, F16>, ogrid, 256, 0, stream, q, ldq, gsg, Sop, zop, r_q, N, H,
+                    eps, inv_C, out, ldo);
     else
-      SANA_LAUNCH("out", out_bf16<HPWG, false, true, F16><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, nullptr, N,
-                                                                                    H, eps, inv_C, out, ldo));
+      launch_kernel("out", out_bf16<HPWG, false, true, F16>, ogrid, 256, 0, stream, q, ldq, gsg, Sop, zop, nullptr, N,
+                    H, eps, inv_C, out, ldo);
     return hipGetLastError();
   }
   constexpr int HPW = 18;
   if (H <= 4 * HPW) {
     const dim3 ogrid((N + 15) / 16, B, 1);
     if (p.norm)
-      SANA_LAUNCH("out", out_bf16<HPW, true, false, F16><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, nullptr, N, H, eps,
-                                                                              inv_C, out, ldo));
+      launch_kernel("out", out_bf16<HPW, true, false, F16>, ogrid, 256, 0, stream, q, ldq, gsg, Sop, zop, nullptr, N, H,
+                    eps, inv_C, out, ldo);
     else
-      SANA_LAUNCH("out", out_bf16<HPW, false, false, F16><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, nullptr, N, H,
-                                                                               eps, inv_C, out, ldo));
+      launch_kernel("out", out_bf16<HPW, false, false, F16>, ogrid, 256, 0, stream, q, ldq, gsg, Sop, zop, nullptr, N,
+                    H, eps, inv_C, out, ldo);
   } else {
     const dim3 ogrid((N + 15) / 16, B, (H + 4 * HPW - 1) / (4 * HPW));
     if (p.norm) {
-      SANA_LAUNCH("rowstats_q", rowstats_kernel<uint16_t, F16><<<rs_blocks, 256, 0, stream>>>(q, ldq, rows, C, eps, r_q));
-      SANA_LAUNCH("out", out_bf16<HPW, true, true, F16><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, r_q, N, H, eps,
-                                                                             inv_C, out, ldo));
+      launch_kernel("rowstats_q", rowstats_kernel<uint16_t, F16>, rs_blocks, 256, 0, stream, q, ldq, rows, C, eps, r_q,
+                    nullptr, 0, nullptr);
+      launch_kernel("out", out_bf16<HPW, true, true, F16>, ogrid, 256, 0, stream, q, ldq, gsg, Sop, zop, r_q, N, H, eps,
+                    inv_C, out, ldo);
     } else {
-      SANA_LAUNCH("out", out_bf16<HPW, false, true, F16><<<ogrid, 256, 0, stream>>>(q, ldq, gsg, Sop, zop, nullptr, N, H,
-                                                                              eps, inv_C, out, ldo));
+      launch_kernel("out", out_bf16<HPW, false, true, F16>, ogrid, 256, 0, stream, q, ldq, gsg, Sop, zop, nullptr, N, H,
+                    eps, inv_C, out, ldo);
     }
   }
   return hipGetLastError();

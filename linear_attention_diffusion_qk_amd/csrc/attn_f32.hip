@@ -147,23 +147,24 @@ hipError_t launch_attn_f32(const AttnPlan& p, const float* q, int64_t ldq, const
   const int B = p.B, N = p.N, H = p.H, C = H * kHeadDim;
   const int64_t rows = (int64_t)B * N;
   if (p.norm)
-    SANA_LAUNCH("rowstats_k", rowstats_kernel<float><<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(k, ldkv, rows, C,
-                                                                                                     eps, r_k));
+    launch_kernel("rowstats_k", rowstats_kernel<float>, (unsigned)((rows + 3) / 4), 256, 0, stream, k, ldkv, rows, C,
+                  eps, r_k, nullptr, 0, nullptr);
   const dim3 grid(p.NC, H, B);
   if (p.norm)
-    SANA_LAUNCH("kv_partial", kv_partial_f32<true><<<grid, 256, 0, stream>>>(k, v, ldkv, r_k, gk, N, H, p.Tc, p.NC, part));
+    launch_kernel("kv_partial", kv_partial_f32<true>, grid, 256, 0, stream, k, v, ldkv, r_k, gk, N, H, p.Tc, p.NC,
+                  part);
   else
-    SANA_LAUNCH("kv_partial", kv_partial_f32<false><<<grid, 256, 0, stream>>>(k, v, ldkv, nullptr, nullptr, N, H, p.Tc,
-                                                                              p.NC, part));
+    launch_kernel("kv_partial", kv_partial_f32<false>, grid, 256, 0, stream, k, v, ldkv, nullptr, nullptr, N, H, p.Tc,
+                  p.NC, part);
   const int64_t elems = (int64_t)B * H * kPartStride;
-  SANA_LAUNCH("kv_reduce", kv_reduce_f32<<<(unsigned)((elems + 255) / 256), 256, 0, stream>>>(part, p.NC, (int64_t)B * H,
-                                                                                                S32, z));
+  launch_kernel("kv_reduce", kv_reduce_f32, (unsigned)((elems + 255) / 256), 256, 0, stream, part, p.NC, (int64_t)B * H,
+                S32, z);
   const dim3 ogrid((N + 3) / 4, B);
   const size_t lds = (size_t)4 * C * sizeof(float);
   if (p.norm)
-    SANA_LAUNCH("out", out_f32<true><<<ogrid, 256, lds, stream>>>(q, ldq, gq, S32, z, N, H, eps, out, ldo));
+    launch_kernel("out", out_f32<true>, ogrid, 256, lds, stream, q, ldq, gq, S32, z, N, H, eps, out, ldo);
   else
-    SANA_LAUNCH("out", out_f32<false><<<ogrid, 256, lds, stream>>>(q, ldq, nullptr, S32, z, N, H, eps, out, ldo));
+    launch_kernel("out", out_f32<false>, ogrid, 256, lds, stream, q, ldq, nullptr, S32, z, N, H, eps, out, ldo);
   return hipGetLastError();
 }
 

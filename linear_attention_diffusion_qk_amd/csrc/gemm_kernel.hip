@@ -413,9 +413,9 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int C, int8_t* xq, fl
                              bool k_blocked) {
   if (C % 8 != 0 || (k_blocked && C % 64 != 0)) return hipErrorInvalidValue;
   if (k_blocked)
-    SANA_LAUNCH("quant_rows", quant_rows_kernel<true><<<(unsigned)((M + 3) / 4), 256, 0, stream>>>(x, M, C, xq, s_x));
+    launch_kernel("quant_rows", quant_rows_kernel<true>, (unsigned)((M + 3) / 4), 256, 0, stream, x, M, C, xq, s_x);
   else
-    SANA_LAUNCH("quant_rows", quant_rows_kernel<false><<<(unsigned)((M + 3) / 4), 256, 0, stream>>>(x, M, C, xq, s_x));
+    launch_kernel("quant_rows", quant_rows_kernel<false>, (unsigned)((M + 3) / 4), 256, 0, stream, x, M, C, xq, s_x);
   return hipGetLastError();
 }
 
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(256) void relayout_k32_kernel(const uint16_t* __res
 hipError_t launch_relayout_k32(const uint16_t* x, int64_t M, int K, uint16_t* xb, hipStream_t stream) {
   if (K % 32 != 0 || M > (1LL << 30) || K / 256 >= 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((M + 63) / 64), (unsigned)((K / 32 + 7) / 8));
-  SANA_LAUNCH("relayout_x", relayout_k32_kernel<<<grid, 256, 0, stream>>>(x, M, K, xb));
+  launch_kernel("relayout_x", relayout_k32_kernel, grid, 256, 0, stream, x, M, K, xb);
   return hipGetLastError();
 }
 
@@ -460,7 +460,7 @@ __global__ __launch_bounds__(256) void pack_k64_kernel(const int8_t* __restrict_
 hipError_t launch_pack_k64(const int8_t* src, int64_t rows, int C, int8_t* dst, hipStream_t stream) {
   if (C % 64 != 0) return hipErrorInvalidValue;
   const int64_t units = rows * (C / 16);
-  SANA_LAUNCH("pack_k64", pack_k64_kernel<<<(unsigned)((units + 255) / 256), 256, 0, stream>>>(src, rows, C, dst));
+  launch_kernel("pack_k64", pack_k64_kernel, (unsigned)((units + 255) / 256), 256, 0, stream, src, rows, C, dst);
   return hipGetLastError();
 }
 
@@ -471,9 +471,8 @@ hipError_t launch_qkv_gemm(const uint16_t* xb, const uint16_t* w, uint16_t* qkv,
   const int mblocks = (int)((M + BM - 1) / BM), nblocks = (NO + BN - 1) / BN;
   const int slab = mblocks >= 8 ? (mblocks + 7) / 8 : 0;
   const int64_t blocks = slab > 0 ? (int64_t)8 * slab * nblocks : (int64_t)mblocks * nblocks;
-  SANA_LAUNCH("qkv_gemm", qkv_gemm_kernel<false, false><<<(unsigned)blocks, kThreads, 0, stream>>>(
-                              xb, w, nullptr, nullptr, qkv, (int)M, C, NO, mblocks, nblocks, slab, k_ssq,
-                              qkv_gemm_k_parts(C)));
+  launch_kernel("qkv_gemm", qkv_gemm_kernel<false, false>, (unsigned)blocks, kThreads, 0, stream, xb, w, nullptr,
+                nullptr, qkv, (int)M, C, NO, mblocks, nblocks, slab, k_ssq, qkv_gemm_k_parts(C));
   return hipGetLastError();
 }
 
@@ -485,11 +484,11 @@ hipError_t launch_gemm_bf16(const uint16_t* xb, const uint16_t* w, uint16_t* y, 
   const int slab = mblocks >= 8 ? (mblocks + 7) / 8 : 0;
   const int64_t blocks = slab > 0 ? (int64_t)8 * slab * nblocks : (int64_t)mblocks * nblocks;
   if (y_blocked)
-    SANA_LAUNCH(label, qkv_gemm_kernel<false, true><<<(unsigned)blocks, kThreads, 0, stream>>>(
-                            xb, w, nullptr, nullptr, y, (int)M, K, NO, mblocks, nblocks, slab, nullptr, 0));
+    launch_kernel(label, qkv_gemm_kernel<false, true>, (unsigned)blocks, kThreads, 0, stream, xb, w, nullptr, nullptr,
+                  y, (int)M, K, NO, mblocks, nblocks, slab, nullptr, 0);
   else
-    SANA_LAUNCH(label, qkv_gemm_kernel<false, false><<<(unsigned)blocks, kThreads, 0, stream>>>(
-                            xb, w, nullptr, nullptr, y, (int)M, K, NO, mblocks, nblocks, slab, nullptr, 0));
+    launch_kernel(label, qkv_gemm_kernel<false, false>, (unsigned)blocks, kThreads, 0, stream, xb, w, nullptr, nullptr,
+                  y, (int)M, K, NO, mblocks, nblocks, slab, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -500,9 +499,8 @@ hipError_t launch_qkv_gemm_i8(const int8_t* xq, const int8_t* wt, const float* s
   const int mblocks = (int)((M + BM - 1) / BM), nblocks = (NO + BN - 1) / BN;
   const int slab = mblocks >= 8 ? (mblocks + 7) / 8 : 0;
   const int64_t blocks = slab > 0 ? (int64_t)8 * slab * nblocks : (int64_t)mblocks * nblocks;
-  SANA_LAUNCH("qkv_gemm_i8", qkv_gemm_kernel<true, false><<<(unsigned)blocks, kThreads, 0, stream>>>(
-                                 xq, wt, s_x, s_w, qkv, (int)M, C, NO, mblocks, nblocks, slab, k_ssq,
-                                 qkv_gemm_k_parts(C)));
+  launch_kernel("qkv_gemm_i8", qkv_gemm_kernel<true, false>, (unsigned)blocks, kThreads, 0, stream, xq, wt, s_x, s_w,
+                qkv, (int)M, C, NO, mblocks, nblocks, slab, k_ssq, qkv_gemm_k_parts(C));
   return hipGetLastError();
 }
 

@@ -197,11 +197,11 @@ hipError_t launch_mix_ffn(const uint16_t* x, const uint16_t* w1, const uint16_t*
   const int rows_per_block = (Hg + bands - 1) / bands;
   const dim3 grid(chunks, B, (Hg + rows_per_block - 1) / rows_per_block);
   if (Wg <= 64)
-    SANA_LAUNCH("dwconv_glu", dwconv_glu_kernel<4><<<grid, kThreads, lds, stream>>>(hbuf, kdw, gbuf, Hg, Wg, F,
-                                                                                  rows_per_block));
+    launch_kernel("dwconv_glu", dwconv_glu_kernel<4>, grid, kThreads, lds, stream, hbuf, kdw, gbuf, Hg, Wg, F,
+                  rows_per_block);
   else
-    SANA_LAUNCH("dwconv_glu", dwconv_glu_kernel<8><<<grid, kThreads, lds, stream>>>(hbuf, kdw, gbuf, Hg, Wg, F,
-                                                                                  rows_per_block));
+    launch_kernel("dwconv_glu", dwconv_glu_kernel<8>, grid, kThreads, lds, stream, hbuf, kdw, gbuf, Hg, Wg, F,
+                  rows_per_block);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_gemm_bf16(gbuf, w2, out, M, F, C, stream, "gemm_project");

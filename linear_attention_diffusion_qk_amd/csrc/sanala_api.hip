@@ -138,22 +138,19 @@ thread_local Timing g_timing;
 }  // namespace
 
 namespace sanala {
-void timing_begin(const char* name, hipStream_t s) {
+bool timing_slot(const char* name, hipEvent_t* begin, hipEvent_t* end) {
   Timing& T = g_timing;
-  if (!T.enabled) return;
+  if (!T.enabled) return false;
   if (T.count == (int)T.slots.size()) {
     TimedKernel k{name, nullptr, nullptr};
-    if (hipEventCreate(&k.begin) != hipSuccess || hipEventCreate(&k.end) != hipSuccess) return;
+    if (hipEventCreate(&k.begin) != hipSuccess || hipEventCreate(&k.end) != hipSuccess) return false;
     T.slots.push_back(k);
   }
-  T.slots[T.count].name = name;
-  (void)hipEventRecord(T.slots[T.count].begin, s);
-}
-void timing_end(hipStream_t s) {
-  Timing& T = g_timing;
-  if (!T.enabled || T.count >= (int)T.slots.size()) return;
-  (void)hipEventRecord(T.slots[T.count].end, s);
-  ++T.count;
+  TimedKernel& k = T.slots[T.count++];
+  k.name = name;
+  *begin = k.begin;
+  *end = k.end;
+  return true;
 }
 }  // namespace sanala
 
