@@ -177,10 +177,10 @@ const char* sana_status_string(sana_status_t status);
 /*
  * Measurement support for benchmarks and profilers (not part of the method).
  *
- * sana_timing_enable(1) makes every later call from the calling host thread record a HIP event pair
- * on its stream around each kernel it launches; sana_timing_enable(0) stops it.  Events are created
- * once per thread and reused.  Recording adds a little host and queue overhead, so throughput runs
- * leave timing off.
+ * sana_timing_enable(1) makes every later call from the calling host thread launch each kernel with a
+ * start/stop HIP event pair that the kernel's own dispatch timestamps (hipExtLaunchKernelGGL), so the
+ * durations are the kernels' own; sana_timing_enable(0) stops it.  Events are created once per thread
+ * and reused.  Timing adds a little host overhead per launch, so throughput runs leave it off.
  *
  * sana_timing_last waits for the events of the most recent call on this thread and writes, for up
  * to `capacity` kernels in launch order, a static kernel name (names may be NULL) and the kernel's

@@ -190,7 +190,7 @@ def quantize_rows_i8(x: torch.Tensor):
 
 
 def sana_timing_enable(enable: bool) -> None:
-    """Record a HIP event pair around every kernel of later calls from this thread (measurement only)."""
+    """Time every kernel of later calls from this thread by its dispatch's start/stop events (measurement only)."""
     _lib.load_library().sana_timing_enable(1 if enable else 0)
 
 
