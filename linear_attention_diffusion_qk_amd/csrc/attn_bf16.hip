@@ -428,7 +428,7 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
         for (int j = 0; j < 2; ++j) {
           const int r = 8 * j + tok8;
           const uint32_t off = (r < rows && h < H) ? (uint32_t)((r * ldo + h * kHeadDim + kg * 8) * 2) : kOutOfRange;
-          buffer_store16(orsrc, off, st[j]);
+          buffer_store16_nt(orsrc, off, st[j]);
         }
       }
     }
@@ -543,7 +543,7 @@ __global__ __launch_bounds__(256) void out_bf16(const uint16_t* __restrict__ q, 
       const uint16_t* zh = zop + bh * kZopPerHead + kg * 8;
       const u32x4 o = head_out<F16>(qr[i], sg, as_bf16x8(load16(sh)), as_bf16x8(load16(sh + 512)), load16(zh),
                                load16(zh + kHeadDim), epsr, (lane & 1) == 0);
-      if (n < N) store16(out + (row0 + n) * ldo + h * kHeadDim + kg * 8, o);
+      if (n < N) store16_nt(out + (row0 + n) * ldo + h * kHeadDim + kg * 8, o);
     }
   }
 }
