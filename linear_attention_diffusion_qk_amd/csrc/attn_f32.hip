@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void out_f32(const float* __restrict__ q, int6
       num = fmaf(pq, S[dd * kHeadDim + e], num);
       den = fmaf(pq, zz[dd], den);
     }
-    __builtin_nontemporal_store(num / (den + eps), &out[row * ldo + h * kHeadDim + e]);
+    out[row * ldo + h * kHeadDim + e] = num / (den + eps);
   }
 }
 
