@@ -281,30 +281,39 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const void* __restri
   wait_vm<0>();  // no load into LDS outlives the block
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the last (unused) operand reads have returned
 
-  // Stores (I8: after the scaling by s_x[m] and s_w[n]), and (k_ssq) per-row sums of squares of the
-  // stored bf16 values that fall in the K block
-  // [K, 2K) (K = C here).  A 32-column tile lies wholly inside or outside that block (C is a multiple of
-  // 32), and v_dot2_f32_bf16 squares the packed pairs being stored; the lane sum (tiles, then
-  // quads in order) is combined with the other column half of the wave (lanes l, l + 32) and then with
-  // the other wave of the same rows through LDS, always in that order.
+  // The output tile goes through LDS so that its global stores are whole runs: each wave first writes
+  // its accumulators as bf16 (I8: after the scaling by s_x[m] and s_w[n]) into a [256][192] image held
+  // in the stage buffers (rows 64g..64g+63 in buffer g, 400-byte row pitch), then the block stores the
+  // image 16 bytes per lane: 384-byte row runs for row-major y, 1 KB runs (16 rows x 64 bytes of one
+  // 32-column chunk) for the chunk-major layout.  With k_ssq, the per-row sums of squares of the stored
+  // bf16 values that fall in the K block [K, 2K) (K = C here) are formed on the way: a 32-column tile
+  // lies wholly inside or outside that block (C is a multiple of 32), and v_dot2_f32_bf16 squares the
+  // packed pairs; the lane sum (tiles, then quads in order) is combined with the other column half of
+  // the wave (lanes l, l + 32) and then with the other wave of the same rows through LDS, always in that
+  // order.
+  constexpr int kOutPitch = BN * 2 + 16;
+  char* const obuf[4] = {stage_buf<0>(), stage_buf<1>(), stage_buf<2>(), stage_buf<3>()};
+  __syncthreads();  // every wave has read its last operands: the stage buffers are free
   const int nb_k0 = K / BN;
   const bool row_ssq = k_ssq && nb >= nb_k0 && nb <= (2 * K - 1) / BN;
   float ss[4] = {0.f, 0.f, 0.f, 0.f};
   // acc[nt][mt] lane l, register 4q + i: row m = 32 mt + l % 32, column n = 32 nt + 8q + 4(l / 32) + i.
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    const int m = m0 + 128 * wm + 32 * mt + (lane & 31);
-    if (m >= M) continue;
-    const float sxm = I8 ? s_x[m] : 1.f;
+    const int rl = 128 * wm + 32 * mt + (lane & 31);  // row within the tile
+    const int m = m0 + rl;
+    const float sxm = I8 ? s_x[min(m, M - 1)] : 1.f;
+    char* const orow = obuf[rl >> 6] + (rl & 63) * kOutPitch;
 #pragma unroll
     for (int nt = 0; nt < 3; ++nt) {
-      const int ntile = n0 + 96 * wn + 32 * nt;
-      const bool in_k = row_ssq && ntile >= K && ntile < 2 * K;
+      const int cl0 = 96 * wn + 32 * nt;
+      const bool in_k = row_ssq && m < M && n0 + cl0 >= K && n0 + cl0 < 2 * K;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = ntile + 8 * q + 4 * (lane >> 5);
+        const int cl = cl0 + 8 * q + 4 * (lane >> 5);
         float v4[4];
         if constexpr (I8) {
+          const int n = n0 + cl;
           const f32x4 sw = n < NO ? loadf4(s_w + n) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int i = 0; i < 4; ++i) v4[i] = ((float)acc[nt][mt][4 * q + i] * sxm) * sw[i];
@@ -314,19 +323,30 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const void* __restri
         }
         const uint32_t p0 = cvt_pk_bf16(v4[0], v4[1]);
         const uint32_t p1 = cvt_pk_bf16(v4[2], v4[3]);
-        if (n < NO) {
-          // n % 4 == 0, so the 4 columns stay inside one 32-column chunk of the blocked layout.
-          uint32_t* dst = reinterpret_cast<uint32_t*>(
-              Y_BLK ? y + (((int64_t)(n >> 5) * M + m) << 5) + (n & 31) : y + (int64_t)m * NO + n);
-          dst[0] = p0;
-          dst[1] = p1;
-        }
+        *reinterpret_cast<uint2*>(orow + cl * 2) = make_uint2(p0, p1);
         if (in_k) ss[mt] = dot2_bf16(p1, p1, dot2_bf16(p0, p0, ss[mt]));
       }
     }
   }
+  __syncthreads();
+  const int rows = min(BM, M - m0), cols = min(BN, NO - n0);  // cols: a multiple of 8
+  if constexpr (Y_BLK) {
+    // Chunk j of the tile: rows x 64 bytes, consecutive in y.
+    for (int i = tid; i < (BN / 32) * BM * 4; i += kThreads) {
+      const int j = i / (BM * 4), r = (i / 4) % BM, w = i & 3;
+      if (r < rows && 32 * j < cols)
+        store16(y + ((((int64_t)(n0 >> 5) + j) * M + m0 + r) << 5) + 8 * w,
+                load16(obuf[r >> 6] + (r & 63) * kOutPitch + (32 * j + 8 * w) * 2));
+    }
+  } else {
+    for (int i = tid; i < BM * (BN / 8); i += kThreads) {
+      const int r = i / (BN / 8), c = i % (BN / 8);
+      if (r < rows && 8 * c < cols)
+        store16(y + (int64_t)(m0 + r) * NO + n0 + 8 * c, load16(obuf[r >> 6] + (r & 63) * kOutPitch + c * 16));
+    }
+  }
   if (row_ssq) {
-    __syncthreads();  // the stage buffers are free
+    __syncthreads();  // the image has been stored: stage buffer 0 is free
     float* red = reinterpret_cast<float*>(g_stage0);  // [2 column halves of the block][256 rows]
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
