@@ -168,7 +168,7 @@ def time_steps(inputs: Inputs, sanala, steps: int, warmup: int) -> float:
 
 
 def kernel_times(inputs: Inputs, sanala, reps: int = 20):
-    """Average per-kernel duration from HIP events the library records on the call's stream."""
+    """Average per-kernel duration from the start/stop events of each kernel's own dispatch (library timing)."""
     sanala.sana_timing_enable(True)
     acc = {}
     try:
