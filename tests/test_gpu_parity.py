@@ -320,3 +320,22 @@ def test_scratch_reuse_across_streams_and_growth(gpu_lib):
     for name, out in outs:
         ref = ref_small if name == "small" else ref_large
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), name
+
+
+def test_chunk_reduction_across_consecutive_calls(gpu_lib):
+    """A sample's state split over many chunks (partials in the per-stream scratch, then the reduction):
+    consecutive calls on one stream with different inputs each match the oracle (nothing of the previous
+    call's state survives), and repeating the first input repeats its output bit for bit."""
+    def run():
+        outs = []
+        for inp in (a, b, a):
+            outs.append(run_attn(gpu_lib, inp))
+        return outs
+
+    for dtype in ("bf16", "f16"):
+        a = gen_attn(51, 2, 3000, dtype=dtype)
+        b = gen_attn(52, 2, 3000, dtype=dtype)
+        o_a, o_b, o_a2 = _with_env("SANA_KV_CHUNK", "256", run)
+        check(o_a, oracle_out(a), a.v, dtype, f"{dtype} first call")
+        check(o_b, oracle_out(b), b.v, dtype, f"{dtype} second call")
+        assert torch.equal(o_a.view(torch.int16), o_a2.view(torch.int16))
