@@ -94,6 +94,10 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int C, int8_t* xq, fl
 // false when timing is off.
 bool timing_slot(const char* name, hipEvent_t* begin, hipEvent_t* end);
 
+// Raises `kernel`'s dynamic-LDS limit to `bytes` on the current device, once per (kernel, device);
+// safe to call from several host threads.
+hipError_t ensure_max_lds(const void* kernel, int bytes);
+
 // kernel<<<grid, block, lds, stream>>>(args...).  With timing on, the launch goes through
 // hipExtLaunchKernelGGL with a start/stop event pair that the dispatch itself timestamps, so the
 // recorded duration is the kernel's own (no event packets between kernels).

@@ -615,14 +615,10 @@ static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t l
     const int per_arg = p.out_strided ? 0 : per;  // 0: strided tiles
     const size_t lds = out_persist_lds_bytes(H);
     const int nw = ((H + 1) / 2 + kPersistPPW - 1) / kPersistPPW;
-    static bool attr_set = false;  // one flag per storage type
-    if (!attr_set) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&out_persist_bf16<kPersistPPW, true, F16>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&out_persist_bf16<kPersistPPW, false, F16>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      attr_set = true;
-    }
+    const hipError_t ea =
+        p.norm ? ensure_max_lds(reinterpret_cast<const void*>(&out_persist_bf16<kPersistPPW, true, F16>), 160 * 1024)
+               : ensure_max_lds(reinterpret_cast<const void*>(&out_persist_bf16<kPersistPPW, false, F16>), 160 * 1024);
+    if (ea != hipSuccess) return ea;
     if (p.norm)
       launch_kernel("out", out_persist_bf16<kPersistPPW, true, F16>, nblk, nw * 64, lds, stream, q, ldq, gsg, Sop, zop,
                     B, N, H, eps, inv_C, out, ldo, per_arg);

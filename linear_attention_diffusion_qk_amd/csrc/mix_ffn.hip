@@ -181,14 +181,9 @@ hipError_t launch_mix_ffn(const uint16_t* x, const uint16_t* w1, const uint16_t*
   e = launch_gemm_bf16(gbuf, w1, hbuf, M, C, 2 * F, stream, "gemm_expand", true);
   if (e != hipSuccess) return e;
   const size_t lds = (size_t)3 * ((Wg + 3) / 4 * 4 + 2) * kTokBytes;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&dwconv_glu_kernel<4>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&dwconv_glu_kernel<8>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr_set = true;
-  }
+  e = Wg <= 64 ? ensure_max_lds(reinterpret_cast<const void*>(&dwconv_glu_kernel<4>), 160 * 1024)
+              : ensure_max_lds(reinterpret_cast<const void*>(&dwconv_glu_kernel<8>), 160 * 1024);
+  if (e != hipSuccess) return e;
   // Row bands: enough blocks for about three rounds of two blocks per CU (each band re-reads one grid
   // row above and below it), bands of at least 8 rows.
   const int chunks = (F + kCh - 1) / kCh;

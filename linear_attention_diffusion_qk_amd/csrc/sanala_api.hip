@@ -138,6 +138,20 @@ thread_local Timing g_timing;
 }  // namespace
 
 namespace sanala {
+hipError_t ensure_max_lds(const void* kernel, int bytes) {
+  static std::mutex mu;
+  static std::vector<std::pair<const void*, int>> done;  // (kernel, device) pairs already raised
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  for (const auto& d : done)
+    if (d.first == kernel && d.second == dev) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.emplace_back(kernel, dev);
+  return e;
+}
+
 bool timing_slot(const char* name, hipEvent_t* begin, hipEvent_t* end) {
   Timing& T = g_timing;
   if (!T.enabled) return false;
