@@ -315,7 +315,7 @@ __device__ __forceinline__ u32x4 swap_halves(u32x4 old, u32x4 src) {
 // operations).  The row sums of squares are combined across waves through LDS in a fixed order.
 // ---------------------------------------------------------------------------------------------
 template <int PPW, bool NORM, bool F16>
-__global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restrict__ q, int64_t ldq,
+__global__ __launch_bounds__(768) void out_persist_bf16(const uint16_t* __restrict__ q, int64_t ldq,
                                                         const uint32_t* __restrict__ gsg,
                                                         const uint16_t* __restrict__ Sop,
                                                         const uint16_t* __restrict__ zop, int B, int N, int H, float eps,
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
   uint16_t* Ss = reinterpret_cast<uint16_t*>(smem);                          // [H][kOpPerHead]
   uint16_t* Zs = Ss + (size_t)H * kOpPerHead;                                // [H][kZopPerHead]
   uint32_t* Gs = reinterpret_cast<uint32_t*>(Zs + (size_t)H * kZopPerHead);  // [H][kSgnPerHead]
-  float* ssq = reinterpret_cast<float*>(Gs + (size_t)H * kSgnPerHead);       // [2][8 waves][16]
+  float* ssq = reinterpret_cast<float*>(Gs + (size_t)H * kSgnPerHead);       // [2][kPersistMaxWaves][16]
 
   const int NW = blockDim.x >> 6;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(512) void out_persist_bf16(const uint16_t* __restri
           for (int u = 0; u < 4; ++u) ss = dot2_h<F16>(bq[i][u], bq[i][u], ss);
         }
       ss = sum_over_lane_groups(ss);
-      float* sb = ssq + (k & 1) * 8 * 16;
+      float* sb = ssq + (k & 1) * kPersistMaxWaves * 16;
       if (kg == 0) sb[w * 16 + n16] = ss;
       __syncthreads();
       float tot = 0.f;
@@ -553,14 +553,12 @@ __global__ __launch_bounds__(256) void out_bf16(const uint16_t* __restrict__ q, 
 // ---------------------------------------------------------------------------------------------
 
 size_t out_persist_lds_bytes(int H) {
-  return (size_t)H * (kOpPerHead * 2 + kZopPerHead * 2 + kSgnPerHead * 4) + 2 * 8 * 16 * 4;
+  return (size_t)H * (kOpPerHead * 2 + kZopPerHead * 2 + kSgnPerHead * 4) + 2 * kPersistMaxWaves * 16 * 4;
 }
 
 size_t bf16_operand_bytes(int64_t BH, int H) {
   return (size_t)BH * (kOpPerHead + kZopPerHead) * 2 + (size_t)H * kSgnPerHead * 4;
 }
-
-constexpr int kPersistPPW = 5;  // head pairs per wave in the persistent output kernel (<= 8 waves: H <= 80)
 
 template <bool F16>
 static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t ldq, const uint16_t* k,
@@ -615,6 +613,7 @@ static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t l
     const int per_arg = p.out_strided ? 0 : per;  // 0: strided tiles
     const size_t lds = out_persist_lds_bytes(H);
     const int nw = ((H + 1) / 2 + kPersistPPW - 1) / kPersistPPW;
+    if (nw > kPersistMaxWaves) return hipErrorInvalidValue;  // the planner never picks this kernel then
     const hipError_t ea =
         p.norm ? ensure_max_lds(reinterpret_cast<const void*>(&out_persist_bf16<kPersistPPW, true, F16>), 160 * 1024)
                : ensure_max_lds(reinterpret_cast<const void*>(&out_persist_bf16<kPersistPPW, false, F16>), 160 * 1024);

@@ -80,7 +80,7 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
   // fill the device (SANA_OUT_KERNEL=2 asks for the tile kernel).
   const int64_t tiles = (int64_t)B * ((N + 15) / 16);
   const int out_env = env_int("SANA_OUT_KERNEL", 0);
-  if (bf && H <= 80 && out_persist_lds_bytes(H) <= kMaxLds && tiles >= 2 * p.num_cus && out_env != kOutTile &&
+  if (bf && H <= 2 * kPersistPPW * kPersistMaxWaves && out_persist_lds_bytes(H) <= kMaxLds && tiles >= 2 * p.num_cus && out_env != kOutTile &&
       out_env != kOutTileGroups)
     p.out_kind = kOutPersist;
   else if (bf && ((tiles < 2 * p.num_cus && out_env != kOutTile) || out_env == kOutTileGroups))
