@@ -31,6 +31,8 @@ struct AttnPlan {
   int NC;               // number of chunks per sample
   int out_kind;         // bf16 output kernel: kOutPersist, kOutTile or kOutTileGroups
   bool out_strided;     // persistent output kernel: block b takes tiles b, b + G, ... (else a contiguous run)
+  int out_group;        // persistent output kernel, not strided: g > 0 blocks share each sample's tiles, block
+                        // j of a sample taking tiles j, j + g, ... (0: each block a contiguous run)
   int num_cus;          // compute units of the current device
   size_t off_rk, off_rq, off_part, off_S32, off_z, off_Sop;
   size_t ws_bytes;

@@ -335,12 +335,28 @@ __global__ __launch_bounds__(768) void out_persist_bf16(const uint16_t* __restri
   const int64_t total = (int64_t)B * tiles_per_sample;
   const int G = gridDim.x;
   // Tiles t < lim belong to this block's sequence; t >= lim means "none".
-  // tiles_per_block = 0: tiles b, b + G, b + 2G, ... (all blocks sweep the tensor together).
-  const bool strided = tiles_per_block == 0;
-  const int64_t T0 = strided ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * tiles_per_block;
-  const int64_t lim = strided ? total : min(total, T0 + tiles_per_block);
+  // tiles_per_block = 0: tiles b, b + G, b + 2G, ... (all blocks sweep the tensor together);
+  // tiles_per_block = -g: blocks [s*g, s*g + g) share sample s, block s*g + j taking its tiles j, j + g,
+  // j + 2g, ... (the group sweeps the sample together); tiles_per_block > 0: a contiguous run.
+  const bool strided = tiles_per_block == 0, grouped = tiles_per_block < 0;
+  int64_t T0, lim, tile_step;
+  if (strided) {
+    T0 = blockIdx.x;
+    lim = total;
+    tile_step = G;
+  } else if (grouped) {
+    const int g = -tiles_per_block;
+    const int64_t s = blockIdx.x / g;
+    T0 = s * tiles_per_sample + blockIdx.x % g;
+    lim = min(total, (s + 1) * tiles_per_sample);
+    tile_step = g;
+  } else {
+    T0 = (int64_t)blockIdx.x * tiles_per_block;
+    lim = min(total, T0 + tiles_per_block);
+    tile_step = 1;
+  }
   if (T0 >= lim) return;
-  const int64_t T1 = strided ? T0 + G : T0 + 1;
+  const int64_t T1 = T0 + tile_step;
 
   // Raw loads of one tile: qr[2*i + j] = load j of pair w*PPW + i; all zero, without memory traffic,
   // for rows past N and for t >= lim.  Head indices are clamped into the row; lanes past N or H are
@@ -433,7 +449,6 @@ __global__ __launch_bounds__(768) void out_persist_bf16(const uint16_t* __restri
       }
     }
   };
-  const int64_t tile_step = strided ? G : 1;
 
   u32x4 qa[2 * PPW], qb[2 * PPW];
   {
@@ -609,8 +624,9 @@ static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t l
     const int64_t tiles = (int64_t)B * ((N + 15) / 16);
     const int blocks = (int)std::min<int64_t>(num_cus, tiles);
     const int per = (int)((tiles + blocks - 1) / blocks);
-    const int nblk = p.out_strided ? blocks : (int)((tiles + per - 1) / per);
-    const int per_arg = p.out_strided ? 0 : per;  // 0: strided tiles
+    // Strided over the tensor, grouped per sample, or contiguous runs (kernel argument 0, -g, run).
+    const int nblk = p.out_strided ? blocks : p.out_group > 0 ? B * p.out_group : (int)((tiles + per - 1) / per);
+    const int per_arg = p.out_strided ? 0 : p.out_group > 0 ? -p.out_group : per;
     const size_t lds = out_persist_lds_bytes(H);
     const int nw = ((H + 1) / 2 + kPersistPPW - 1) / kPersistPPW;
     if (nw > kPersistMaxWaves) return hipErrorInvalidValue;  // the planner never picks this kernel then

@@ -92,6 +92,14 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
   {
     const int64_t blocks = std::min<int64_t>(p.num_cus, tiles);
     p.out_strided = p.out_kind == kOutPersist && (N + 15) / 16 >= 2 * blocks && env_int("SANA_OUT_SCHED", 2) != 1;
+    // Otherwise, when a sample's tiles split evenly into runs of the per-block count, the blocks of a
+    // sample take its tiles interleaved, so that they too sweep the sample together (SANA_OUT_SCHED=1
+    // asks for plain contiguous runs).
+    const int64_t per = blocks > 0 ? (tiles + blocks - 1) / blocks : 1;
+    const int tps = (N + 15) / 16;
+    p.out_group = p.out_kind == kOutPersist && !p.out_strided && env_int("SANA_OUT_SCHED", 2) != 1 && tps % per == 0
+                      ? (int)(tps / per)
+                      : 0;
   }
   const size_t BH = (size_t)B * H;
   size_t off = 0;

@@ -241,11 +241,13 @@ def test_many_heads_tile_kernel_with_row_statistics_of_q(gpu_lib):
     check(run_attn(gpu_lib, inp), oracle_out(inp), inp.v, "bf16", "H=80 N=8200")
 
 
-@pytest.mark.parametrize("B,N,norm", [(1, 12345, True), (2, 8200, True), (1, 9000, False)])
+@pytest.mark.parametrize("B,N,norm", [(1, 12345, True), (2, 8200, True), (1, 9000, False), (8, 1024, True),
+                                      (9, 1000, False)])
 def test_persistent_schedules_agree(gpu_lib, B, N, norm):
-    """Persistent output kernel with strided tiles (the default at these sizes) and with contiguous
-    runs: every tile written (NaN-poisoned output), both bit-identical, within the gates.  Covers a
-    ragged last tile, a sample change inside the strided sweep and the norm-off variant."""
+    """Persistent output kernel with its default schedule (strided tiles for the long samples; for
+    8 x 1024 and 9 x 1000 the blocks of a sample taking its tiles interleaved) and with contiguous runs:
+    every tile written (NaN-poisoned output), both bit-identical, within the gates.  Covers a ragged
+    last tile, a sample change inside the strided sweep and the norm-off variant."""
     inp = gen_attn(47 + N, B, N, dtype="bf16", norm=norm)
     q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
     gq, gk = gains_dev(inp.gq), gains_dev(inp.gk)
