@@ -345,9 +345,12 @@ __global__ __launch_bounds__(768) void out_persist_bf16(const uint16_t* __restri
     lim = total;
     tile_step = G;
   } else if (grouped) {
+    // Consecutive block ids go to the 8 XCDs in turn; when the grid divides evenly, ids are remapped
+    // so that the blocks of a sample share an XCD (and its L2 copy of the sample's S', z').
     const int g = -tiles_per_block;
-    const int64_t s = blockIdx.x / g;
-    T0 = s * tiles_per_sample + blockIdx.x % g;
+    const int lb = G % 8 == 0 ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    const int64_t s = lb / g;
+    T0 = s * tiles_per_sample + lb % g;
     lim = min(total, (s + 1) * tiles_per_sample);
     tile_step = g;
   } else {
