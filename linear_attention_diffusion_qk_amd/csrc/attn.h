@@ -20,7 +20,7 @@ constexpr int kPersistPPW = 3;
 constexpr int kPersistMaxWaves = 12;
 constexpr int kOutPersist = 1;  // bf16 output: one block per CU, all heads, operands in LDS
 constexpr int kOutTile = 2;     // bf16 output: 16-token tiles over all heads, operands from global memory
-constexpr int kOutTileGroups = 3;  // bf16 output for few tiles: 16 tokens x 20 heads per block, r_q from the
+constexpr int kOutTileGroups = 3;  // bf16 output for few tiles: 16 tokens x 8 heads per block, r_q from the
                                    // row-statistics launch (which then covers Q and K)
 
 // Launch plan and scratch layout of one attention call.
