@@ -117,3 +117,53 @@ def test_w8a8_qkv_within_quantisation_bound_of_fp64_projection():
     err = np.abs(got - ref)
     assert np.all(err <= bound)
     assert err.max() > 0  # the quantisation is not a no-op
+
+
+def _identity_quant_case(seed, B, N, H, D):
+    """x with integer entries in [-127, 127] and row maximum 127, so the per-token quantiser is exactly
+    the identity (s_x = 127/127 = 1, codes = x).  Wt_q holds 64 * (a permutation matrix) in each of the
+    q, k and v row blocks, with column scales 1/64, 2/64, 3/64 (powers of two times small integers, so
+    every product below is exact in fp32 and fp64).  The W8A8 projection is then exactly
+    q = x, k = 2 x[:, pk], v = 3 x[:, pv]."""
+    rng = np.random.default_rng(seed)
+    C = H * D
+    x = rng.integers(-127, 128, size=(B, N, C)).astype(np.float32)
+    rows = x.reshape(-1, C)
+    at = rng.integers(0, C, size=rows.shape[0])
+    rows[np.arange(rows.shape[0]), at] = np.where(rng.random(rows.shape[0]) < 0.5, 127.0, -127.0)
+    perms = [np.arange(C), rng.permutation(C), rng.permutation(C)]
+    wt_q = np.zeros((3 * C, C), np.int8)
+    for blk, p in enumerate(perms):
+        wt_q[blk * C + np.arange(C), p] = 64
+    sw = np.concatenate([np.full(C, (blk + 1) / 64.0, np.float32) for blk in range(3)])
+    return x, wt_q, sw, perms
+
+
+def test_w8a8_composition_matches_linear_attn_of_exact_projection():
+    """qkv_w8a8_linear_attn = linear_attn of the dequantised projection's q | k | v blocks, in that order
+    (the Sana notes, section 7: W8A8 projection, linear attention in full precision).  With the
+    identity quantisation above, the expected q, k, v are known in closed form; a k|v or q|k slice swap,
+    raw x in place of the projection, or a projection left without its scales each move the output by
+    far more than rounding."""
+    H, D, eps = 2, 32, 1e-6
+    x, wt_q, sw, (pq, pk, pv) = _identity_quant_case(5, 2, 7, H, D)
+    xq, sx = oracle.quantize_rows(x)
+    assert np.array_equal(xq.astype(np.float32), x) and np.all(sx == 1.0)
+    rng = np.random.default_rng(6)
+    C = H * D
+    for gq, gk in ((1 + 0.1 * rng.standard_normal(C), 1 + 0.1 * rng.standard_normal(C)), (None, None)):
+        gq = None if gq is None else gq.astype(np.float32)
+        gk = None if gk is None else gk.astype(np.float32)
+        got = oracle.qkv_w8a8_linear_attn(x, wt_q, sw, gq, gk, H, D, eps)
+        q, k, v = x[..., pq], 2.0 * x[..., pk], 3.0 * x[..., pv]
+        want = oracle.linear_attn(q, k, v, gq, gk, H, D, eps)
+        assert np.max(np.abs(got - want)) <= 1e-14 * np.max(np.abs(want))
+        scale = np.max(np.abs(want))
+        wrong = {
+            "k|v swapped": oracle.linear_attn(q, v, k, gq, gk, H, D, eps),
+            "q|k swapped": oracle.linear_attn(k, q, v, gq, gk, H, D, eps),
+            "raw x": oracle.linear_attn(x, x, x, gq, gk, H, D, eps),
+            "no dequantisation": oracle.linear_attn(64 * q, 64 * x[..., pk], 64 * x[..., pv], gq, gk, H, D, eps),
+        }
+        for name, o in wrong.items():
+            assert np.max(np.abs(o - got)) > 1e-3 * scale, name
