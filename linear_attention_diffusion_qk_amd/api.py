@@ -32,22 +32,58 @@ def _stream_handle(stream, like: Optional[torch.Tensor] = None) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _check_dev(*ts):
-    for t in ts:
-        if t is None:
-            continue
-        if not t.is_cuda:
-            raise ValueError("libsanala takes device tensors")
+_NAMES_OF_DTYPE = {v: k for k, v in _DTYPES.items()}
+
+
+def _need(specs, device_of=None):
+    """Checks (name, tensor, numel, dtype) tuples before anything reaches the C-ABI: the kernels read and
+    write exactly `numel` elements of `dtype` behind each pointer, so a short, mistyped, strided or
+    foreign-device tensor would be read or written out of bounds.  Shape and dtype are checked first,
+    then contiguity, then that every tensor is a device tensor on one device.  A tensor of None is
+    skipped (optional gains)."""
+    present = [(n, t, k, d) for n, t, k, d in specs if t is not None]
+    for name, t, numel, dtype in present:
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch.Tensor")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+        if t.numel() != numel:
+            raise ValueError(f"{name} must hold {numel} elements, got {t.numel()} (shape {tuple(t.shape)})")
+    for name, t, _, _ in present:
         if not t.is_contiguous():
-            raise ValueError("libsanala takes contiguous tensors")
+            raise ValueError(f"{name} must be contiguous")
+    ref = device_of if device_of is not None else (present[0][1] if present else None)
+    for name, t, _, _ in present:
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor (libsanala takes device pointers)")
+        if ref is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _need_sizes(**sizes):
+    for name, v in sizes.items():
+        if int(v) < 1:
+            raise ValueError(f"{name} must be >= 1, got {v}")
+
+
+def _same_as(name, t, like):
+    if not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(like.shape) or t.dtype != like.dtype:
+        raise ValueError(f"{name} must be a {like.dtype} tensor of shape {tuple(like.shape)}")
 
 
 def sana_linear_attn_fwd(q, k, v, gq, gk, B: int, N: int, H: int, D: int, eps: float, out,
                          stream=None, dtype: Optional[int] = None) -> None:
     """Same arguments as the C entry point; tensors stand in for the device pointers."""
-    _check_dev(q, k, v, gq, gk, out)
     if dtype is None:
+        if not isinstance(q, torch.Tensor) or q.dtype not in _DTYPES:
+            raise ValueError("q must be a float32, bfloat16 or float16 tensor")
         dtype = _DTYPES[q.dtype]
+    if int(dtype) not in _NAMES_OF_DTYPE:
+        raise ValueError(f"unknown dtype code {dtype}")
+    _need_sizes(B=B, N=N, H=H, D=D)
+    tdt, n, C = _NAMES_OF_DTYPE[int(dtype)], int(B) * int(N) * int(H) * int(D), int(H) * int(D)
+    _need([("q", q, n, tdt), ("k", k, n, tdt), ("v", v, n, tdt), ("out", out, n, tdt),
+           ("gq", gq, C, torch.float32), ("gk", gk, C, torch.float32)])
     lib = _lib.load_library()
     st = lib.sana_linear_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gq), _ptr(gk), int(B), int(N), int(H), int(D),
                                   float(eps), _ptr(out), _stream_handle(stream, q), int(dtype))
@@ -57,7 +93,12 @@ def sana_linear_attn_fwd(q, k, v, gq, gk, B: int, N: int, H: int, D: int, eps: f
 
 def sana_qkv_linear_attn_fwd(x, Wqkv, gq, gk, B: int, N: int, H: int, D: int, eps: float, out,
                              stream=None) -> None:
-    _check_dev(x, Wqkv, gq, gk, out)
+    _need_sizes(B=B, N=N, H=H, D=D)
+    C = int(H) * int(D)
+    n = int(B) * int(N) * C
+    bf = torch.bfloat16
+    _need([("x", x, n, bf), ("Wqkv", Wqkv, C * 3 * C, bf), ("out", out, n, bf), ("gq", gq, C, torch.float32),
+           ("gk", gk, C, torch.float32)])
     lib = _lib.load_library()
     st = lib.sana_qkv_linear_attn_fwd(_ptr(x), _ptr(Wqkv), _ptr(gq), _ptr(gk), int(B), int(N), int(H), int(D),
                                       float(eps), _ptr(out), _stream_handle(stream, x))
@@ -66,7 +107,8 @@ def sana_qkv_linear_attn_fwd(x, Wqkv, gq, gk, B: int, N: int, H: int, D: int, ep
 
 
 def sana_pack_weight_i8(Wt_q, rows: int, C: int, Wt_p, stream=None) -> None:
-    _check_dev(Wt_q, Wt_p)
+    _need_sizes(rows=rows, C=C)
+    _need([("Wt_q", Wt_q, int(rows) * int(C), torch.int8), ("Wt_p", Wt_p, int(rows) * int(C), torch.int8)])
     lib = _lib.load_library()
     st = lib.sana_pack_weight_i8(_ptr(Wt_q), int(rows), int(C), _ptr(Wt_p), _stream_handle(stream, Wt_q))
     if st != _lib.SANA_OK:
@@ -75,7 +117,12 @@ def sana_pack_weight_i8(Wt_q, rows: int, C: int, Wt_p, stream=None) -> None:
 
 def sana_qkv_w8a8_linear_attn_fwd(x, Wt_p, w_scale, gq, gk, B: int, N: int, H: int, D: int, eps: float, out,
                                   stream=None) -> None:
-    _check_dev(x, Wt_p, w_scale, gq, gk, out)
+    _need_sizes(B=B, N=N, H=H, D=D)
+    C = int(H) * int(D)
+    n = int(B) * int(N) * C
+    bf = torch.bfloat16
+    _need([("x", x, n, bf), ("Wt_p", Wt_p, 3 * C * C, torch.int8), ("w_scale", w_scale, 3 * C, torch.float32),
+           ("out", out, n, bf), ("gq", gq, C, torch.float32), ("gk", gk, C, torch.float32)])
     lib = _lib.load_library()
     st = lib.sana_qkv_w8a8_linear_attn_fwd(_ptr(x), _ptr(Wt_p), _ptr(w_scale), _ptr(gq), _ptr(gk), int(B), int(N),
                                            int(H), int(D), float(eps), _ptr(out), _stream_handle(stream, x))
@@ -84,7 +131,9 @@ def sana_qkv_w8a8_linear_attn_fwd(x, Wt_p, w_scale, gq, gk, B: int, N: int, H: i
 
 
 def sana_quantize_rows_i8(x, rows: int, C: int, xq, x_scale, stream=None) -> None:
-    _check_dev(x, xq, x_scale)
+    _need_sizes(rows=rows, C=C)
+    _need([("x", x, int(rows) * int(C), torch.bfloat16), ("xq", xq, int(rows) * int(C), torch.int8),
+           ("x_scale", x_scale, int(rows), torch.float32)])
     lib = _lib.load_library()
     st = lib.sana_quantize_rows_i8(_ptr(x), int(rows), int(C), _ptr(xq), _ptr(x_scale), _stream_handle(stream, x))
     if st != _lib.SANA_OK:
@@ -92,7 +141,11 @@ def sana_quantize_rows_i8(x, rows: int, C: int, xq, x_scale, stream=None) -> Non
 
 
 def sana_mix_ffn_fwd(x, W1, Wdw, W2, B: int, Hg: int, Wg: int, C: int, F: int, out, stream=None) -> None:
-    _check_dev(x, W1, Wdw, W2, out)
+    _need_sizes(B=B, Hg=Hg, Wg=Wg, C=C, F=F)
+    n = int(B) * int(Hg) * int(Wg) * int(C)
+    bf = torch.bfloat16
+    _need([("x", x, n, bf), ("W1", W1, int(C) * 2 * int(F), bf), ("Wdw", Wdw, 2 * int(F) * 9, bf),
+           ("W2", W2, int(F) * int(C), bf), ("out", out, n, bf)])
     lib = _lib.load_library()
     st = lib.sana_mix_ffn_fwd(_ptr(x), _ptr(W1), _ptr(Wdw), _ptr(W2), int(B), int(Hg), int(Wg), int(C), int(F),
                               _ptr(out), _stream_handle(stream, x))
@@ -116,6 +169,7 @@ def linear_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gq: Optional[
             raise ValueError("gains must be float32 of length H*D")
     if out is None:
         out = torch.empty_like(q)
+    _same_as("out", out, q)
     sana_linear_attn_fwd(q, k, v, gq, gk, B, N, H, D, eps, out)
     return out
 
@@ -130,6 +184,7 @@ def qkv_linear_attn(x: torch.Tensor, Wqkv: torch.Tensor, gq: Optional[torch.Tens
         raise ValueError("shape mismatch between x, Wqkv and H*D")
     if out is None:
         out = torch.empty_like(x)
+    _same_as("out", out, x)
     sana_qkv_linear_attn_fwd(x, Wqkv, gq, gk, B, N, H, D, eps, out)
     return out
 
@@ -158,6 +213,7 @@ def qkv_w8a8_linear_attn(x: torch.Tensor, Wt_p: torch.Tensor, w_scale: torch.Ten
         raise ValueError("shape mismatch between x, Wt_p, w_scale and H*D")
     if out is None:
         out = torch.empty_like(x)
+    _same_as("out", out, x)
     sana_qkv_w8a8_linear_attn_fwd(x, Wt_p, w_scale, gq, gk, B, N, H, D, eps, out)
     return out
 
@@ -173,6 +229,7 @@ def mix_ffn(x: torch.Tensor, W1: torch.Tensor, Wdw: torch.Tensor, W2: torch.Tens
         raise ValueError("shape mismatch between x, W1, Wdw, W2 and the grid")
     if out is None:
         out = torch.empty_like(x)
+    _same_as("out", out, x)
     sana_mix_ffn_fwd(x, W1, Wdw, W2, B, Hg, Wg, C, F, out)
     return out
 

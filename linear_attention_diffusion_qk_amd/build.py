@@ -51,7 +51,11 @@ def build(verbose: bool = False) -> str:
         cmd = [hipcc, *HIPFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        _run(cmd)
+        r = _run(cmd)
+        # The host pass does not know the packed-fp32 target feature and says so; anything else is shown.
+        warn = [ln for ln in (r.stderr or "").splitlines() if "warning" in ln and "packed-fp32-ops" not in ln]
+        if warn:
+            print(f"{src}:\n" + "\n".join(warn), flush=True)
         return obj
 
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:

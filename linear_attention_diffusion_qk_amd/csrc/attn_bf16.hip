@@ -215,6 +215,18 @@ __global__ __launch_bounds__(256, 5) void kv_state_bf16(const uint16_t* __restri
   }
 }
 
+// r[row] = 1 / sqrt(sum_j part[row * nparts + j] / C + eps): the QK-Norm scale from per-row partial
+// sums of squares over column panels (summed in panel order), one thread per row.
+__global__ __launch_bounds__(256) void rowfinish_kernel(const float* __restrict__ part, int nparts, int64_t rows,
+                                                        float inv_C, float eps, float* __restrict__ r) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= rows) return;
+  const float* p = part + row * nparts;
+  float ss = 0.f;
+  for (int j = 0; j < nparts; ++j) ss += p[j];
+  r[row] = 1.0f / sqrtf(ss * inv_C + eps);
+}
+
 // One thread per state element (b, h, i): sum of the chunk partials in chunk order (8 loads in flight
 // per step), then the output kernel's operands.
 template <bool NORM>

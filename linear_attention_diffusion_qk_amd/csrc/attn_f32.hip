@@ -160,7 +160,12 @@ hipError_t launch_attn_f32(const AttnPlan& p, const float* q, int64_t ldq, const
   launch_kernel("kv_reduce", kv_reduce_f32, (unsigned)((elems + 255) / 256), 256, 0, stream, part, p.NC, (int64_t)B * H,
                 S32, z);
   const dim3 ogrid((N + 3) / 4, B);
-  const size_t lds = (size_t)4 * C * sizeof(float);
+  const size_t lds = (size_t)4 * C * sizeof(float);  // up to 160 KB at H = 320
+  if (lds > 64 * 1024) {
+    const hipError_t ea = p.norm ? ensure_max_lds(reinterpret_cast<const void*>(&out_f32<true>), (int)lds)
+                                 : ensure_max_lds(reinterpret_cast<const void*>(&out_f32<false>), (int)lds);
+    if (ea != hipSuccess) return ea;
+  }
   if (p.norm)
     launch_kernel("out", out_f32<true>, ogrid, 256, lds, stream, q, ldq, gq, S32, z, N, H, eps, out, ldo);
   else

@@ -66,16 +66,4 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ x, 
   if (lane == 0) r[row] = 1.0f / sqrtf(ss / (float)C + eps);
 }
 
-// r[row] = 1 / sqrt(sum_j part[row * nparts + j] / C + eps): the QK-Norm scale from per-row partial
-// sums of squares over column panels (summed in panel order), one thread per row.
-static __global__ __launch_bounds__(256) void rowfinish_kernel(const float* __restrict__ part, int nparts, int64_t rows,
-                                                        float inv_C, float eps, float* __restrict__ r) {
-  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (row >= rows) return;
-  const float* p = part + row * nparts;
-  float ss = 0.f;
-  for (int j = 0; j < nparts; ++j) ss += p[j];
-  r[row] = 1.0f / sqrtf(ss * inv_C + eps);
-}
-
 }  // namespace sanala

@@ -76,6 +76,8 @@ def test_mix_ffn_argument_errors(gpu_lib):
     with pytest.raises(gpu_lib.SanaError) as e:
         gpu_lib.sana_mix_ffn_fwd(x, w1, kdw, w2, 1, 2, 2, 64, 48, out)
     assert e.value.status == 2
+    wide = gen_mix_ffn(10, 1, 1, 300, C=64, F=64)   # Wg > 128 (checked before any use)
+    x, w1, kdw, w2 = (dev(a, "bf16") for a in (wide.x, wide.w1, wide.kdw, wide.w2))
     with pytest.raises(gpu_lib.SanaError) as e:
-        gpu_lib.sana_mix_ffn_fwd(x, w1, kdw, w2, 1, 1, 300, 64, 64, out)   # Wg > 128 (checked before any use)
+        gpu_lib.sana_mix_ffn_fwd(x, w1, kdw, w2, 1, 1, 300, 64, 64, torch.empty_like(x))
     assert e.value.status == 2
