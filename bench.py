@@ -9,7 +9,8 @@ host cores as a CPU baseline.
 A step is one sana_linear_attn_fwd call over the resident inputs (row statistics, KV state, chunk
 reduction and output: the whole path).
 
-  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload config4|config2|config3|config5|w8a8|mixffn]
+  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload config4|config1|config2|config3|config5|w8a8|mixffn]
+                  [--no-cold] [--no-secondary] [--no-cpu-baseline]
   python bench.py --mode copy        # plain device copy of known size (counter calibration under rocprofv3)
   python bench.py --summarize-traffic KERNEL_FETCH.db KERNEL_WRITE.db COPY_FETCH.db COPY_WRITE.db
                                      # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE databases -> profiles/hbm_traffic.txt
@@ -31,6 +32,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
 MFMA_I8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA peak
 
 WORKLOADS = {
+    "config1": dict(cfg=1, desc="512px linear attention, fp32: B=1, N=256 (16x16 latent), H=70, D=32, fp32 I/O, "
+                                "QK-RMSNorm on"),
     "config4": dict(cfg=4, desc="4K linear attention: B=1, N=16384 (128x128 latent), H=70, D=32, bf16 I/O, "
                                 "K ~ N(0,30^2) with 1% rows x100, QK-RMSNorm on"),
     "config2": dict(cfg=2, desc="1024px linear attention: B=1, N=1024 (32x32 latent), H=70, D=32, bf16 I/O, QK-RMSNorm on"),
@@ -95,7 +98,8 @@ class Inputs:
         bf = torch.bfloat16
         g = lambda a: torch.from_numpy(a).to("cuda")  # noqa: E731
         if self.kind == "attn":
-            self.q, self.k, self.v = (torch.from_numpy(a).to("cuda").to(bf) for a in (inp.q, inp.k, inp.v))
+            tdt = torch.float32 if inp.dtype == "f32" else bf
+            self.q, self.k, self.v = (torch.from_numpy(a).to("cuda").to(tdt) for a in (inp.q, inp.k, inp.v))
             self.out = torch.empty_like(self.q)
         elif self.kind == "qkv":
             self.x = torch.from_numpy(inp.x).to("cuda").to(bf)
@@ -136,12 +140,16 @@ class Inputs:
             sanala.sana_qkv_w8a8_linear_attn_fwd(self.x, self.wt, self.sw, self.gq, self.gk, self.B, self.N, self.H,
                                                  self.D, self.host.eps, self.out)
 
+    @property
+    def esize(self) -> int:
+        return 4 if getattr(self.host, "dtype", "bf16") == "f32" else 2
+
     def algorithmic_bytes(self) -> int:
-        """Read Q, K, V and write O once: 4 * B * N * C * 2 bytes (bf16)."""
-        return 4 * self.B * self.N * self.C * 2
+        """Read Q, K, V and write O once: 4 * B * N * C * element size bytes."""
+        return 4 * self.B * self.N * self.C * self.esize
 
     def kernel_bytes(self, kernel: str) -> float:
-        tok = self.B * self.N * self.C * 2
+        tok = self.B * self.N * self.C * self.esize
         if kernel in ("kv_state", "kv_partial"):
             return 2 * tok            # read K and V
         if kernel == "out":
@@ -165,6 +173,91 @@ def time_steps(inputs: Inputs, sanala, steps: int, warmup: int) -> float:
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps  # ms per step
+
+
+class CacheFlush:
+    """A read-only pass over 1 GiB between timed calls: evicts the L2s and the 256 MB Infinity Cache and
+    leaves only clean lines behind (a write pass would leave dirty lines whose write-back lands on the
+    next kernels).  Runs outside the timing events."""
+
+    def __init__(self, nbytes: int = 1 << 30):
+        import torch
+        self.buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        self.sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        import torch
+        torch.sum(self.buf, dim=0, out=self.sink)
+
+
+def time_cold(inputs: Inputs, sanala, steps: int, warmup: int, flush: CacheFlush) -> float:
+    """ms per call with the caches flushed before every call (flush outside the events): the inputs
+    come from HBM, as when the call follows unrelated work."""
+    import torch
+    for _ in range(warmup):
+        flush()
+        inputs.step(sanala)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in evs:
+        flush()
+        e0.record()
+        inputs.step(sanala)
+        e1.record()
+    torch.cuda.synchronize()
+    return sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+
+
+def copy_ceiling(reps: int = 20):
+    """Measured bandwidth ceilings beside the 8 TB/s spec: a plain device-to-device copy of 256 MiB
+    (torch's copy kernel; reads and writes 256 MiB each) and a read-only reduction over 1 GiB."""
+    import torch
+    n = 256 * 1024 * 1024
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    big = torch.ones((1 << 30) // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    out = {}
+    for name, fn, nbytes in (("copy", lambda: dst.copy_(src), 2 * n), ("read", lambda: torch.sum(big, dim=0, out=sink), 1 << 30)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[f"{name}_GBps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    out["note"] = ("device copy of 256 MiB (bytes read + written) and a read-only sum over 1 GiB, torch kernels, "
+                   f"{reps} back-to-back launches each; spec peak {HBM_PEAK_GBPS:.0f} GB/s")
+    del src, dst, big
+    return out
+
+
+def point(inputs: Inputs, ms: float) -> dict:
+    b = inputs.algorithmic_bytes()
+    gbps = b / (ms * 1e-3) / 1e9
+    return {"ms_per_step": round(ms, 5), "tokens_per_s": round(inputs.B * inputs.N / (ms * 1e-3), 1),
+            "achieved_GBps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
+def host_cpu() -> dict:
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "usable_cpus": affinity}
 
 
 def kernel_times(inputs: Inputs, sanala, reps: int = 20):
@@ -206,9 +299,11 @@ def cpu_baseline(inputs: Inputs, min_seconds: float = 12.0, max_reps: int = 200)
         if el >= min_seconds or reps >= max_reps:
             break
     tokens = h.B * h.N * reps
-    return {"value": tokens / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{reps} full passes of the {inputs.name} workload ({h.B}x{h.N} tokens each) "
-                      f"through the fp64 NumPy oracle in {el:.1f}s"}
+    res = {"value": tokens / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{reps} full passes of the {inputs.name} workload ({h.B}x{h.N} tokens each) "
+                     f"through the fp64 NumPy oracle in {el:.1f}s; cores = the BLAS threads it ran on"}
+    res.update(host_cpu())
+    return res
 
 
 def run_copy_calibration():
@@ -285,6 +380,7 @@ def main():
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cold", action="store_true", help="skip the flushed-cache timings and the copy ceiling")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -310,6 +406,14 @@ def main():
     alg_bytes = main_in.algorithmic_bytes()
     call_gbps = alg_bytes / (ms * 1e-3) / 1e9
     log(f"[bench] {args.workload}: {ms * 1e3:.1f} us/step, {value:.4g} tokens/s, {call_gbps:.0f} GB/s algorithmic")
+    cold = None
+    flush = None
+    if not args.no_cold and main_in.kind in ("attn", "qkv", "w8a8"):
+        flush = CacheFlush()
+        cms = time_cold(main_in, sanala, args.steps, max(1, args.warmup // 2), flush)
+        cold = point(main_in, cms)
+        cold["note"] = "1 GiB read-only pass before every call, outside the events"
+        log(f"[bench] {args.workload} cold: {cms * 1e3:.1f} us/step")
 
     kt = kernel_times(main_in, sanala)
     log(f"[bench] per-kernel (events): " + ", ".join(f"{k}={v * 1e3:.1f}us" for k, v in kt.items()))
@@ -347,20 +451,29 @@ def main():
     if not args.no_secondary and args.workload == "config4":
         sec_in = Inputs("config2")
         sms = time_steps(sec_in, sanala, max(args.steps, 50), args.warmup)
-        sb = sec_in.algorithmic_bytes()
-        secondary = {"workload": WORKLOADS["config2"]["desc"], "tokens_per_s": round(sec_in.B * sec_in.N / (sms * 1e-3)),
-                     "ms_per_step": round(sms, 5), "achieved_GBps": round(sb / (sms * 1e-3) / 1e9, 1),
-                     "frac_of_hbm_peak": round(sb / (sms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                     "note": "18 MB working set: stays in the 256 MB Infinity Cache across back-to-back steps"}
-        log(f"[bench] config2: {sms * 1e3:.1f} us/step")
+        secondary = {"workload": WORKLOADS["config2"]["desc"], "warm": point(sec_in, sms)}
+        secondary["warm"]["note"] = ("back-to-back calls: the 18 MB working set stays in the 256 MB Infinity Cache, "
+                                     "so this is not an HBM figure")
+        log(f"[bench] config2: {sms * 1e3:.1f} us/step warm")
+        if flush is not None:
+            scms = time_cold(sec_in, sanala, max(args.steps, 50), args.warmup, flush)
+            secondary["cold"] = point(sec_in, scms)
+            secondary["cold"]["note"] = "1 GiB read-only pass before every call, outside the events: inputs from HBM"
+            log(f"[bench] config2: {scms * 1e3:.1f} us/step cold")
+        secondary["kernels_us"] = {k: round(v * 1e3, 2) for k, v in kernel_times(sec_in, sanala).items()}
         del sec_in
+    ceiling = None
+    if not args.no_cold:
+        del flush
+        ceiling = copy_ceiling()
+        log(f"[bench] copy ceiling: {ceiling}")
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(main_in)
     if cpu:
         log(f"[bench] cpu baseline: {cpu['value']:.4g} tokens/s on {cpu['cores']} threads")
 
     line = {
-        "metric": "linear-attn tokens/s (+ achieved HBM GB/s, % of peak) at N=16384; N=1024 in 'secondary'",
+        "metric": "linear-attn tokens/s + achieved HBM GB/s (% of peak) at N=1024 and N=16384",
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -376,6 +489,9 @@ def main():
                    "D": main_in.D, "C": main_in.C, "parallelism": "single GPU"},
         "achieved_GBps": round(call_gbps, 1),
         "frac_of_hbm_peak": round(call_gbps / HBM_PEAK_GBPS, 4),
+        "timing": "value: back-to-back calls (warm); cold: caches flushed before each call",
+        "cold": cold,
+        "copy_ceiling": ceiling,
         "kernels_us": {k: round(v * 1e3, 2) for k, v in kt.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
