@@ -22,13 +22,20 @@
  * Calls are asynchronous on `stream` and return without a host synchronisation.  Argument checks
  * happen on the host before anything is enqueued; faults inside kernels surface at the caller's
  * next synchronisation.  NaN/Inf in the inputs propagate to the outputs they touch; nothing checks
- * for them.  Scratch memory (row statistics, split-N partial states, the reduced state, and for the
- * fused calls the qkv buffer) is one buffer per (device, stream), taken from the device's stream-ordered
- * pool with hipMallocAsync on `stream` the first time and reused by later calls on the same stream
- * (stream order runs them after the earlier calls' kernels); a call that needs more frees it on
- * `stream` and takes a larger one.  Calls on different streams never share scratch; calls from several
- * host threads on one stream are serialised while they enqueue.  The buffers are kept until the process
- * ends.
+ * for them.
+ *
+ * Scratch memory (row statistics, split-N partial states, the reduced state, and for the fused calls
+ * the qkv buffer) is owned by the library: one buffer per (device, stream), taken from the device's
+ * stream-ordered pool with hipMallocAsync on `stream` the first time and reused by later calls on the
+ * same stream (stream order runs them after the earlier calls' kernels); a call that needs more frees
+ * it on `stream` and takes a larger one.  Calls on different streams never share scratch; calls from
+ * several host threads on one stream are serialised while they enqueue.  There is no limit on the
+ * number of streams.  A buffer is kept until sana_release_scratch(stream) frees it (call that before
+ * destroying a stream the library has used) or the process ends.  Every call records an event on its
+ * stream after its work, and the next call on the same buffer makes its stream wait for that event
+ * unless it has completed: if a stream is destroyed without sana_release_scratch and the runtime hands
+ * its handle value to a new stream, the new stream's calls still start only after the old kernels
+ * that used the buffer have finished.
  * Results are bitwise reproducible: every reduction runs in a fixed order, with no floating-point
  * atomics.
  */
@@ -170,6 +177,14 @@ sana_status_t sana_mix_ffn_fwd(const void* x, const void* W1, const void* Wdw, c
  */
 sana_status_t sana_quantize_rows_i8(const void* x, int64_t rows, int C, void* xq, float* x_scale,
                                     hipStream_t stream);
+
+/*
+ * sana_release_scratch -- frees the library's scratch buffer of `stream` on the current device,
+ * stream-ordered (hipFreeAsync on `stream`, so kernels already queued on it finish first), and forgets
+ * the stream.  `stream` must still exist.  A later call on `stream` takes a new buffer.  Returns
+ * SANA_OK (also when the stream has no buffer) or SANA_ERR_HIP if the free fails.
+ */
+sana_status_t sana_release_scratch(hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* sana_status_string(sana_status_t status);

@@ -17,6 +17,7 @@ from .api import (  # noqa: F401
     sana_qkv_linear_attn_fwd,
     sana_qkv_w8a8_linear_attn_fwd,
     sana_quantize_rows_i8,
+    sana_release_scratch,
     sana_timing_enable,
     sana_timing_last,
 )

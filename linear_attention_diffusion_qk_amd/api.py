@@ -153,6 +153,14 @@ def sana_mix_ffn_fwd(x, W1, Wdw, W2, B: int, Hg: int, Wg: int, C: int, F: int, o
         raise SanaError(st, "sana_mix_ffn_fwd")
 
 
+def sana_release_scratch(stream=None) -> None:
+    """Frees the library's scratch buffer of `stream` (default: the current stream) on the current device,
+    stream-ordered; call it before destroying a stream the library has used."""
+    st = _lib.load_library().sana_release_scratch(_stream_handle(stream))
+    if st != _lib.SANA_OK:
+        raise SanaError(st, "sana_release_scratch")
+
+
 def linear_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gq: Optional[torch.Tensor],
                 gk: Optional[torch.Tensor], H: int, D: int = 32, eps: float = 1e-6,
                 out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -34,7 +34,9 @@ struct AttnPlan {
   int out_group;        // persistent output kernel, not strided: g > 0 blocks share each sample's tiles, block
                         // j of a sample taking tiles j, j + g, ... (0: each block a contiguous run)
   int num_cus;          // compute units of the current device
-  size_t off_rk, off_rq, off_part, off_S32, off_z, off_Sop;
+  bool state_xchg;      // 16-bit, QK-Norm on, r_q in the output kernel: r_k formed inside the state pass
+  uint32_t xchg_spin;   // its wait limit, 100 MHz ticks
+  size_t off_rk, off_rq, off_part, off_S32, off_z, off_Sop, off_xchg;
   size_t ws_bytes;
 };
 
@@ -56,6 +58,14 @@ hipError_t launch_attn_bf16(const AttnPlan& p, const uint16_t* q, int64_t ldq, c
                             int64_t ldkv, const float* gq, const float* gk, float eps, uint16_t* out, int64_t ldo,
                             void* ws, int num_cus, hipStream_t stream, const float* k_ssq, int k_parts);
 size_t out_persist_lds_bytes(int H);
+// KV state with r_k formed in the same pass (kv_state_x.hip): tagged exchange buffers of
+// kv_state_x_exchange_bytes(B*N, H) bytes at xchg; epoch unique per call (never 0).
+size_t kv_state_x_exchange_bytes(int64_t rows, int H);
+hipError_t launch_kv_state_x(bool f16, const uint16_t* k, const uint16_t* v, int64_t ld, const float* gq,
+                             const float* gk, int B, int N, int H, int Tc, int NC, float eps, void* xchg,
+                             uint32_t epoch, uint32_t spin_ticks, float* part, uint16_t* Sop, uint16_t* zop,
+                             uint32_t* gsg, hipStream_t stream);
+uint32_t next_epoch();
 size_t bf16_operand_bytes(int64_t BH, int H);
 
 int max_heads();

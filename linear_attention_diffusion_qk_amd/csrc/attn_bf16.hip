@@ -27,47 +27,11 @@
 //             and stream 16-token tiles of Q (two tiles' loads in flight): r_q from the Q rows
 //             held in registers (v_dot2_f32_bf16), a on MFMA, b by v_dot2_f32_bf16.
 #include "rowstats.h"
+#include "state_ops.h"
 
 #include <algorithm>
 
 namespace sanala {
-
-constexpr int kOpPerHead = 2 * 64 * 8;  // S' operand per head: 2 e-blocks x 64 lanes x 8 bf16
-constexpr int kZopPerHead = 2 * kHeadDim;  // z' per head: 32 bf16 hi, then 32 bf16 lo
-constexpr int kSgnPerHead = 16;            // query sign masks per head: 4 lane groups x 4 words
-
-// Position of S'[d][e] inside a head's operand block.  Lane l = m + 16*kg of e-block eb holds
-// S'[8*kg + j][e] (j = 0..7) with e = 8*(m/4) + 4*eb + m%4; with that column order the MFMA result
-// lane (t, kg) receives output channels 8kg..8kg+7 of token t.
-__device__ __forceinline__ int sop_index(int d, int e) {
-  const int m = 4 * (e >> 3) + (e & 3), eb = (e >> 2) & 1, kg = d >> 3, j = d & 7;
-  return eb * 512 + (m + 16 * kg) * 8 + j;
-}
-
-// Sign masks (0x8000 per negative gain) of query dims 8kg + 2u, 8kg + 2u + 1 of head h.
-template <bool NORM>
-__device__ __forceinline__ uint32_t sign_word(const float* __restrict__ gq, int h, int kg, int u) {
-  if (!NORM) return 0u;
-  const int d0 = h * kHeadDim + 8 * kg + 2 * u;
-  return (gq[d0] < 0.f ? 0x8000u : 0u) | (gq[d0 + 1] < 0.f ? 0x80000000u : 0u);
-}
-
-// Writes one reduced state element (i < 1024: S~[i/32][i%32]; else z~[i-1024]) of head h of sample
-// row bh as the output kernel's operands, scaled by G_d = |gq_d| |gk_d| (1 without the norm).
-template <bool NORM>
-__device__ __forceinline__ void emit_state(int64_t bh, int h, int i, float s, const float* __restrict__ gq,
-                                           const float* __restrict__ gk, uint16_t* __restrict__ Sop,
-                                           uint16_t* __restrict__ zop) {
-  const int d = i < kHeadDim * kHeadDim ? i / kHeadDim : i - kHeadDim * kHeadDim;
-  if (NORM) s *= fabsf(gq[h * kHeadDim + d]) * fabsf(gk[h * kHeadDim + d]);
-  if (i < kHeadDim * kHeadDim) {
-    Sop[bh * kOpPerHead + sop_index(d, i % kHeadDim)] = (uint16_t)f32_to_bf16_bits(s);
-  } else {
-    const uint32_t hi = f32_to_bf16_bits(s);
-    zop[bh * kZopPerHead + d] = (uint16_t)hi;
-    zop[bh * kZopPerHead + kHeadDim + d] = (uint16_t)f32_to_bf16_bits(s - __uint_as_float(hi << 16));
-  }
-}
 
 // ---------------------------------------------------------------------------------------------
 // KV state.  Block = 4 waves; block (c, p, b) owns heads 2p, 2p+1 and tokens [c*Tc, min(N, c*Tc+Tc)),
@@ -614,7 +578,12 @@ static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t l
   const float inv_C = 1.0f / (float)C;
   float* r_q = reinterpret_cast<float*>(base + p.off_rq);
   const bool groups = p.out_kind == kOutTileGroups;
-  if (p.norm && groups)  // r_k and r_q in one launch (the output blocks see only some heads of a row)
+  const bool xchg = p.state_xchg && p.norm && !k_ssq && !groups;
+  if (xchg) {
+    const hipError_t e = launch_kv_state_x(F16, k, v, ldkv, gq, gk, B, N, H, p.Tc, p.NC, eps, base + p.off_xchg,
+                                           next_epoch(), p.xchg_spin, part, Sop, zop, gsg, stream);
+    if (e != hipSuccess) return e;
+  } else if (p.norm && groups)  // r_k and r_q in one launch (the output blocks see only some heads of a row)
     launch_kernel("rowstats_kq", rowstats_kernel<uint16_t, F16>, (unsigned)((2 * rows + 3) / 4), 256, 0, stream, k,
                   ldkv, rows, C, eps, r_k, q, ldq, r_q);
   else if (p.norm && k_ssq)
@@ -624,7 +593,8 @@ static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t l
     launch_kernel("rowstats_k", rowstats_kernel<uint16_t, F16>, rs_blocks, 256, 0, stream, k, ldkv, rows, C, eps, r_k,
                   nullptr, 0, nullptr);
   const dim3 grid(p.NC, (H + 1) / 2, B);
-  if (p.norm)
+  if (xchg) {
+  } else if (p.norm)
     launch_kernel("kv_state", kv_state_bf16<true, F16>, grid, 256, 0, stream, k, v, ldkv, r_k, gq, gk, N, H, p.Tc, p.NC,
                   part, Sop, zop, gsg);
   else

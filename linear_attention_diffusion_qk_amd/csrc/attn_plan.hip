@@ -2,6 +2,7 @@
 #include "attn.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 
 namespace sanala {
@@ -28,7 +29,14 @@ int device_cus() {
 }
 }  // namespace
 
-int max_heads() { return 320; }  // the fp32 output kernel stages 4 rows of C floats in LDS
+int max_heads() { return 320; }
+
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{0};
+  uint32_t e = counter.fetch_add(1) + 1;
+  while (e == 0) e = counter.fetch_add(1) + 1;  // 0 is what fresh memory holds
+  return e;
+}  // the fp32 output kernel stages 4 rows of C floats in LDS
 
 AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
   AttnPlan p{};
@@ -101,6 +109,21 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
                       ? (int)(tps / per)
                       : 0;
   }
+  // K row statistics inside the state pass (one read of K), for calls whose output kernel forms r_q
+  // itself: SANA_STATE_XCHG=1 asks for it (off by default: on MI355X it measures slower than the
+  // separate row-statistics pass followed by the plain state pass).  SANA_XCHG_SPIN_US: the exchange's
+  // wait limit in microseconds (default 200; 0 makes every wait that is not met at once take the
+  // local route, which gives the same bits).
+  {
+    const char* s = std::getenv("SANA_STATE_XCHG");
+    const bool on = s && s[0] == '1' && s[1] == 0;
+    p.state_xchg = bf && norm && p.out_kind != kOutTileGroups && on;
+  }
+  {
+    const char* s = std::getenv("SANA_XCHG_SPIN_US");
+    const long us = (s && *s) ? std::atol(s) : 200;
+    p.xchg_spin = (uint32_t)(std::min<long>(std::max<long>(us, 0), 10000000) * 100);
+  }
   const size_t BH = (size_t)B * H;
   size_t off = 0;
   p.off_rk = off;   off = align_up(off + (norm ? (size_t)B * N * 4 : 0), 256);
@@ -110,6 +133,7 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
   p.off_S32 = off;  off = align_up(off + (bf ? 0 : BH * kHeadDim * kHeadDim * 4), 256);
   p.off_z = off;    off = align_up(off + (bf ? 0 : BH * kHeadDim * 4), 256);
   p.off_Sop = off;  off = align_up(off + (bf ? bf16_operand_bytes((int64_t)BH, H) : 0), 256);
+  p.off_xchg = off; off = align_up(off + (p.state_xchg ? kv_state_x_exchange_bytes((int64_t)B * N, H) : 0), 256);
   p.ws_bytes = off;
   return p;
 }

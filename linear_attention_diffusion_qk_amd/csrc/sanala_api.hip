@@ -1,6 +1,7 @@
 // C-ABI entry points of libsanala: argument checks, stream-ordered scratch, launches.
 #include "../../include/sanala.h"
 #include "attn.h"
+#include "scratch_table.h"
 
 #include <hip/hip_runtime.h>
 
@@ -28,73 +29,41 @@ void init_pool(int dev) {
   });
 }
 
-// Scratch kept per (device, stream).  A call on stream s reuses the buffer of the previous call on s:
-// stream order runs this call's kernels after that call's, so no synchronisation is needed.  A call
-// that needs more frees the buffer stream-ordered and allocates a larger one from the device's pool.
-// The lease holds the entry's lock for the whole call, so a growth on one host thread cannot free a
-// buffer that another thread has taken for the same stream but not yet enqueued work on.  (Freeing
-// scratch at every call cost about 15 us of host time per call, more than the 1024-token call's GPU
-// time.)  Buffers live until the process ends.
-struct ScratchEntry {
-  int dev = -1;
-  hipStream_t stream = nullptr;
-  void* ptr = nullptr;
-  size_t bytes = 0;
-  std::mutex mu;
+// Scratch kept per (device, stream): the lifecycle rules are those of ScratchTable (scratch_table.h).
+// (Freeing scratch at every call cost about 15 us of host time per call, more than the 1024-token
+// call's GPU time.)
+struct HipBackend {
+  int alloc_async(void** p, size_t bytes, void* s) {
+    return hipMallocAsync(p, bytes, static_cast<hipStream_t>(s)) == hipSuccess ? 0 : 1;
+  }
+  int free_async(void* p, void* s) { return hipFreeAsync(p, static_cast<hipStream_t>(s)) == hipSuccess ? 0 : 1; }
+  int event_create(void** ev) {
+    // Used only to order later work after it: no timing, and no system-scope cache flush when it fires.
+    return hipEventCreateWithFlags(reinterpret_cast<hipEvent_t*>(ev), hipEventDisableTiming | hipEventDisableSystemFence) ==
+                   hipSuccess
+               ? 0
+               : 1;
+  }
+  int event_record(void* ev, void* s) {
+    return hipEventRecord(static_cast<hipEvent_t>(ev), static_cast<hipStream_t>(s)) == hipSuccess ? 0 : 1;
+  }
+  int event_done(void* ev) { return hipEventQuery(static_cast<hipEvent_t>(ev)) == hipSuccess ? 1 : 0; }
+  int stream_wait(void* s, void* ev) {
+    return hipStreamWaitEvent(static_cast<hipStream_t>(s), static_cast<hipEvent_t>(ev), 0) == hipSuccess ? 0 : 1;
+  }
 };
-constexpr int kMaxScratch = 256;
-ScratchEntry g_scratch[kMaxScratch];
-int g_scratch_used = 0;
-std::mutex g_scratch_mu;
+HipBackend g_backend;
+sanala::ScratchTable<HipBackend> g_table(g_backend);
 
 class ScratchLease {
  public:
-  ScratchLease() = default;
-  ScratchLease(const ScratchLease&) = delete;
-  ScratchLease& operator=(const ScratchLease&) = delete;
-  ~ScratchLease() {
-    if (entry_) entry_->mu.unlock();
-  }
-  // Returns hipSuccess with ptr() valid for work enqueued on `stream`, or an error (nothing held).
   hipError_t acquire(int dev, hipStream_t stream, size_t bytes) {
-    ScratchEntry* e = nullptr;
-    {
-      std::lock_guard<std::mutex> lk(g_scratch_mu);
-      for (int i = 0; i < g_scratch_used; ++i)
-        if (g_scratch[i].dev == dev && g_scratch[i].stream == stream) e = &g_scratch[i];
-      if (!e) {
-        if (g_scratch_used == kMaxScratch) return hipErrorOutOfMemory;
-        e = &g_scratch[g_scratch_used++];
-        e->dev = dev;
-        e->stream = stream;
-      }
-    }
-    e->mu.lock();
-    if (e->bytes < bytes) {
-      if (e->ptr && hipFreeAsync(e->ptr, stream) != hipSuccess) {
-        e->mu.unlock();
-        return hipErrorUnknown;
-      }
-      e->ptr = nullptr;
-      e->bytes = 0;
-      const size_t grown = std::max(bytes, bytes / 4 * 5);
-      const size_t nb = (grown + (2u << 20) - 1) / (2u << 20) * (2u << 20);
-      void* p = nullptr;
-      const hipError_t err = hipMallocAsync(&p, nb, stream);
-      if (err != hipSuccess) {
-        e->mu.unlock();
-        return err;
-      }
-      e->ptr = p;
-      e->bytes = nb;
-    }
-    entry_ = e;
-    return hipSuccess;
+    return g_table.acquire(lease_, dev, stream, bytes) == 0 ? hipSuccess : hipErrorOutOfMemory;
   }
-  void* ptr() const { return entry_ ? entry_->ptr : nullptr; }
+  void* ptr() const { return lease_.ptr(); }
 
  private:
-  ScratchEntry* entry_ = nullptr;
+  sanala::ScratchTable<HipBackend>::Lease lease_;
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -187,6 +156,12 @@ extern "C" int sana_timing_last(const char** names, float* ms, int capacity) {
   return T.count;
 }
 
+extern "C" sana_status_t sana_release_scratch(hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SANA_ERR_HIP;
+  return g_table.release(dev, stream) == 0 ? SANA_OK : SANA_ERR_HIP;
+}
+
 extern "C" const char* sana_status_string(sana_status_t s) {
   switch (s) {
     case SANA_OK: return "ok";
@@ -198,9 +173,9 @@ extern "C" const char* sana_status_string(sana_status_t s) {
   return "unknown status";
 }
 
-extern "C" sana_status_t sana_linear_attn_fwd(const void* q, const void* k, const void* v, const float* gq,
-                                              const float* gk, int B, int N, int H, int D, float eps, void* out,
-                                              hipStream_t stream, sana_dtype_t dtype) {
+namespace {
+sana_status_t check_attn(const void* q, const void* k, const void* v, const float* gq, const float* gk, int B, int N,
+                         int H, int D, float eps, void* out, sana_dtype_t dtype) {
   if (!q || !k || !v || !out) return SANA_ERR_INVALID_ARG;
   if (dtype != SANA_F32 && dtype != SANA_BF16 && dtype != SANA_F16) return SANA_ERR_INVALID_ARG;
   sana_status_t st = check_common(B, N, H, D, eps, gq, gk);
@@ -210,14 +185,26 @@ extern "C" sana_status_t sana_linear_attn_fwd(const void* q, const void* k, cons
   const size_t tbytes = (size_t)B * N * H * D * esz;
   if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, k, tbytes) || overlaps(out, tbytes, v, tbytes))
     return SANA_ERR_INVALID_ARG;
+  return SANA_OK;
+}
+
+int dtype_code(sana_dtype_t dtype) {
+  return dtype == SANA_BF16 ? sanala::kDtypeBf16 : dtype == SANA_F16 ? sanala::kDtypeF16 : sanala::kDtypeF32;
+}
+}  // namespace
+
+extern "C" sana_status_t sana_linear_attn_fwd(const void* q, const void* k, const void* v, const float* gq,
+                                              const float* gk, int B, int N, int H, int D, float eps, void* out,
+                                              hipStream_t stream, sana_dtype_t dtype) {
+  const sana_status_t st = check_attn(q, k, v, gq, gk, B, N, H, D, eps, out, dtype);
+  if (st != SANA_OK) return st;
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return SANA_ERR_HIP;
   init_pool(dev);
   g_timing.count = 0;
   const bool norm = gq != nullptr;
-  const int dt = dtype == SANA_BF16 ? sanala::kDtypeBf16 : dtype == SANA_F16 ? sanala::kDtypeF16 : sanala::kDtypeF32;
-  const sanala::AttnPlan plan = sanala::plan_attn(B, N, H, dt, norm);
+  const sanala::AttnPlan plan = sanala::plan_attn(B, N, H, dtype_code(dtype), norm);
   ScratchLease lease;
   if (lease.acquire(dev, stream, plan.ws_bytes) != hipSuccess) return SANA_ERR_HIP;
   const int64_t C = (int64_t)H * D;

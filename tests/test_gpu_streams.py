@@ -1,0 +1,52 @@
+"""Scratch lifecycle on the GPU: streams created and destroyed one at a time, more of them than any fixed
+table would hold, some released through sana_release_scratch and some destroyed while the library's
+kernels are still queued on them (the runtime may then give the same handle value to the next stream).
+Every output must equal the single-stream result bit for bit."""
+import ctypes
+
+import pytest
+import torch
+
+from synth import gen_attn
+from tests.parity_util import dev, gains_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _hip_runtime():
+    """The HIP runtime this process already loaded (torch's), for stream creation and destruction."""
+    torch.cuda.init()
+    path = next(line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line)
+    hip = ctypes.CDLL(path)
+    hip.hipStreamCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+def test_many_streams_created_and_destroyed(gpu_lib):
+    inp = gen_attn(61, 1, 700, dtype="bf16")
+    q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
+    gq, gk = gains_dev(inp.gq), gains_dev(inp.gk)
+    ref = gpu_lib.linear_attn(q, k, v, gq, gk, inp.H)
+    torch.cuda.synchronize()
+    hip = _hip_runtime()
+    outs, handles = [], set()
+    for i in range(300):
+        s = ctypes.c_void_p()
+        assert hip.hipStreamCreate(ctypes.byref(s)) == 0
+        handles.add(s.value)
+        out = torch.empty_like(q)
+        gpu_lib.sana_linear_attn_fwd(q, k, v, gq, gk, 1, inp.N, inp.H, inp.D, inp.eps, out, stream=s.value)
+        if i % 3 == 0:
+            gpu_lib.sana_release_scratch(stream=s.value)
+        assert hip.hipStreamDestroy(s) == 0   # no synchronisation: kernels may still be queued
+        outs.append(out)
+    torch.cuda.synchronize()
+    print(f"[streams] 300 streams, {len(handles)} distinct handle values", flush=True)
+    for i, out in enumerate(outs):
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"stream {i}"
+    gpu_lib.sana_release_scratch()   # the current stream's buffer; a second release is a no-op
+    gpu_lib.sana_release_scratch()
+    again = gpu_lib.linear_attn(q, k, v, gq, gk, inp.H)   # takes a new buffer
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(torch.int16), ref.view(torch.int16))
