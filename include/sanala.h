@@ -54,7 +54,8 @@ typedef enum {
   SANA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad eps, only one gain NULL, ... */
   SANA_ERR_UNSUPPORTED = 2, /* a shape or dtype the library has no kernel for (D != 32, ...) */
   SANA_ERR_MISALIGNED = 3,  /* a tensor pointer is not 16-byte aligned */
-  SANA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+  SANA_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  SANA_ERR_SCRATCH_LIMIT = 5 /* sana_linear_attn_fwd_noalloc: the call needs more than its static scratch */
 } sana_status_t;
 
 typedef enum {
@@ -82,6 +83,27 @@ sana_status_t sana_linear_attn_fwd(const void* q, const void* k, const void* v,
                                    const float* gq, const float* gk,
                                    int B, int N, int H, int D, float eps,
                                    void* out, hipStream_t stream, sana_dtype_t dtype);
+
+/*
+ * sana_linear_attn_fwd_noalloc -- sana_linear_attn_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * kernels and results (bit for bit) as sana_linear_attn_fwd; the scratch is a static device array of
+ * 64 MiB per GPU, part of the library's code object, which each GPU the library runs on holds until the
+ * process ends.  The call itself allocates nothing: no hipMalloc, hipFree or stream-ordered pool use,
+ * and no timing events (sana_timing_enable does not apply to it).  The caller still passes q, k, v,
+ * gains and out.
+ *
+ * A call whose scratch exceeds 64 MiB returns SANA_ERR_SCRATCH_LIMIT with nothing enqueued (the
+ * 16384-token and the 32 x 1024-token workloads need about 4.4 and 5.0 MB).  Every call on a GPU
+ * shares that GPU's array and leaves its contents behind; nothing in it has to start at any value (each
+ * kernel writes every element it later reads).  Calls that overlap on one GPU (on different streams,
+ * or from several host threads without ordering) race on the array and give undefined results:
+ * serialise them, e.g. on one stream.  Errors otherwise as for sana_linear_attn_fwd.
+ */
+sana_status_t sana_linear_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                                           const float* gq, const float* gk,
+                                           int B, int N, int H, int D, float eps,
+                                           void* out, hipStream_t stream, sana_dtype_t dtype);
 
 /*
  * sana_qkv_linear_attn_fwd -- fused front end: qkv = x @ Wqkv (bf16 MFMA GEMM, fp32 accumulation,

@@ -12,6 +12,7 @@ from .api import (  # noqa: F401
     qkv_w8a8_linear_attn,
     quantize_rows_i8,
     sana_linear_attn_fwd,
+    sana_linear_attn_fwd_noalloc,
     sana_mix_ffn_fwd,
     sana_pack_weight_i8,
     sana_qkv_linear_attn_fwd,

@@ -16,12 +16,13 @@ SANA_ERR_INVALID_ARG = 1
 SANA_ERR_UNSUPPORTED = 2
 SANA_ERR_MISALIGNED = 3
 SANA_ERR_HIP = 4
+SANA_ERR_SCRATCH_LIMIT = 5
 SANA_F32 = 0
 SANA_BF16 = 1
 SANA_F16 = 2
 
 # Every symbol include/sanala.h declares.
-EXPORTS = ("sana_linear_attn_fwd", "sana_qkv_linear_attn_fwd", "sana_qkv_w8a8_linear_attn_fwd",
+EXPORTS = ("sana_linear_attn_fwd", "sana_linear_attn_fwd_noalloc", "sana_qkv_linear_attn_fwd", "sana_qkv_w8a8_linear_attn_fwd",
            "sana_quantize_rows_i8", "sana_pack_weight_i8", "sana_mix_ffn_fwd", "sana_release_scratch",
            "sana_status_string", "sana_timing_enable", "sana_timing_last")
 
@@ -47,6 +48,8 @@ def load_library() -> ctypes.CDLL:
         vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         lib.sana_linear_attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, vp, vp, ci]
         lib.sana_linear_attn_fwd.restype = ci
+        lib.sana_linear_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, vp, vp, ci]
+        lib.sana_linear_attn_fwd_noalloc.restype = ci
         lib.sana_qkv_linear_attn_fwd.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, cf, vp, vp]
         lib.sana_qkv_linear_attn_fwd.restype = ci
         lib.sana_qkv_w8a8_linear_attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, vp, vp]

@@ -91,6 +91,26 @@ def sana_linear_attn_fwd(q, k, v, gq, gk, B: int, N: int, H: int, D: int, eps: f
         raise SanaError(st, "sana_linear_attn_fwd")
 
 
+def sana_linear_attn_fwd_noalloc(q, k, v, gq, gk, B: int, N: int, H: int, D: int, eps: float, out,
+                                 stream=None, dtype: Optional[int] = None) -> None:
+    """sana_linear_attn_fwd on the library's static per-device scratch: the call allocates no device memory."""
+    if dtype is None:
+        if not isinstance(q, torch.Tensor) or q.dtype not in _DTYPES:
+            raise ValueError("q must be a float32, bfloat16 or float16 tensor")
+        dtype = _DTYPES[q.dtype]
+    if int(dtype) not in _NAMES_OF_DTYPE:
+        raise ValueError(f"unknown dtype code {dtype}")
+    _need_sizes(B=B, N=N, H=H, D=D)
+    tdt, n, C = _NAMES_OF_DTYPE[int(dtype)], int(B) * int(N) * int(H) * int(D), int(H) * int(D)
+    _need([("q", q, n, tdt), ("k", k, n, tdt), ("v", v, n, tdt), ("out", out, n, tdt),
+           ("gq", gq, C, torch.float32), ("gk", gk, C, torch.float32)])
+    lib = _lib.load_library()
+    st = lib.sana_linear_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(gq), _ptr(gk), int(B), int(N), int(H),
+                                          int(D), float(eps), _ptr(out), _stream_handle(stream, q), int(dtype))
+    if st != _lib.SANA_OK:
+        raise SanaError(st, "sana_linear_attn_fwd_noalloc")
+
+
 def sana_qkv_linear_attn_fwd(x, Wqkv, gq, gk, B: int, N: int, H: int, D: int, eps: float, out,
                              stream=None) -> None:
     _need_sizes(B=B, N=N, H=H, D=D)

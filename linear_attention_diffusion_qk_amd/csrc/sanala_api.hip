@@ -66,6 +66,32 @@ class ScratchLease {
   sanala::ScratchTable<HipBackend>::Lease lease_;
 };
 
+// Scratch of the allocation-free entry point: one static device array per GPU the library runs on,
+// held until the process ends.  Host code never uses the array's name as an address (on the host it
+// is only a stand-in for the symbol): each device's address comes from hipGetSymbolAddress, taken
+// once per device with that device current.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+__device__ __attribute__((aligned(256))) static char scratch[kStaticScratchBytes];
+
+std::once_flag g_static_once[kMaxDevices];
+void* g_static_ptr[kMaxDevices];
+hipError_t g_static_err[kMaxDevices];
+
+// The current device's address of `scratch`, or nullptr (err set).  `dev` must be the current device.
+void* static_scratch(int dev, hipError_t* err) {
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::call_once(g_static_once[dev], [dev]() {
+    void* p = nullptr;
+    g_static_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_static_ptr[dev] = g_static_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *err = g_static_err[dev];
+  return g_static_ptr[dev];
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -169,6 +195,8 @@ extern "C" const char* sana_status_string(sana_status_t s) {
     case SANA_ERR_UNSUPPORTED: return "unsupported shape or dtype (D must be 32, H <= 320, B <= 65535)";
     case SANA_ERR_MISALIGNED: return "tensor pointer not 16-byte aligned";
     case SANA_ERR_HIP: return "HIP runtime error";
+    case SANA_ERR_SCRATCH_LIMIT:
+      return "the call needs more scratch than the allocation-free entry point's static buffer (64 MiB per device)";
   }
   return "unknown status";
 }
@@ -209,6 +237,28 @@ extern "C" sana_status_t sana_linear_attn_fwd(const void* q, const void* k, cons
   if (lease.acquire(dev, stream, plan.ws_bytes) != hipSuccess) return SANA_ERR_HIP;
   const int64_t C = (int64_t)H * D;
   const hipError_t e = sanala::launch_attn(plan, q, C, k, v, C, gq, gk, eps, out, C, lease.ptr(), stream);
+  return e == hipSuccess ? SANA_OK : SANA_ERR_HIP;
+}
+
+extern "C" sana_status_t sana_linear_attn_fwd_noalloc(const void* q, const void* k, const void* v, const float* gq,
+                                                      const float* gk, int B, int N, int H, int D, float eps,
+                                                      void* out, hipStream_t stream, sana_dtype_t dtype) {
+  const sana_status_t st = check_attn(q, k, v, gq, gk, B, N, H, D, eps, out, dtype);
+  if (st != SANA_OK) return st;
+  const sanala::AttnPlan plan = sanala::plan_attn(B, N, H, dtype_code(dtype), gq != nullptr);
+  if (plan.ws_bytes > kStaticScratchBytes) return SANA_ERR_SCRATCH_LIMIT;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SANA_ERR_HIP;
+  hipError_t e = hipSuccess;
+  void* ws = static_scratch(dev, &e);
+  if (!ws) return SANA_ERR_HIP;
+  // Kernel timing would create events: it stays off for this call.
+  const bool timing = g_timing.enabled;
+  g_timing.enabled = false;
+  g_timing.count = 0;
+  const int64_t C = (int64_t)H * D;
+  e = sanala::launch_attn(plan, q, C, k, v, C, gq, gk, eps, out, C, ws, stream);
+  g_timing.enabled = timing;
   return e == hipSuccess ? SANA_OK : SANA_ERR_HIP;
 }
 
