@@ -59,7 +59,11 @@ __device__ __forceinline__ float unit_ssq(u32x4 w) {
   return ss;
 }
 
-__device__ __forceinline__ float r_from_ssq(float ss, int C, float eps) { return 1.0f / sqrtf(ss / (float)C + eps); }
+// r = 1/sqrt(ss/C + eps) as v_rsq_f32 of ss * (1/C) + eps (about 1 ulp; both routes use it, and a
+// relative error near 1e-7 in r is far below what the 16-bit output keeps).
+__device__ __forceinline__ float r_from_ssq(float ss, float inv_C, float eps) {
+  return __builtin_amdgcn_rsqf(fmaf(ss, inv_C, eps));
+}
 
 // The order in which a token's P head-pair partials are summed (the same on every route): with G the
 // smallest power of two >= min(P, 64), lane s of a G-lane segment adds the partials k = s, s + G,
@@ -99,7 +103,7 @@ __device__ __forceinline__ float seg_butterfly(float x, int G) {
 // r_k of one token from its full row, by one wave: each head pair's partial formed exactly as the
 // state pass forms it (8 lanes per pair), then summed in the order above.  Every lane returns the value.
 template <bool F16>
-__device__ float row_r(const uint16_t* __restrict__ krow, int H, int P, float eps, int lane) {
+__device__ float row_r(const uint16_t* __restrict__ krow, int H, int P, float inv_C, float eps, int lane) {
   const int cu = lane & 7, slot = lane >> 3;
   const int G = seg_lanes(P);
   float acc = 0.f;
@@ -113,7 +117,7 @@ __device__ float row_r(const uint16_t* __restrict__ krow, int H, int P, float ep
       if ((p0 + q) % G == lane) acc += x;
     }
   }
-  return r_from_ssq(__shfl(seg_butterfly(acc, G), 0), H * kHeadDim, eps);
+  return r_from_ssq(__shfl(seg_butterfly(acc, G), 0), inv_C, eps);
 }
 }  // namespace
 
@@ -129,10 +133,12 @@ __global__ __launch_bounds__(256, 2) void kv_state_x(const uint16_t* __restrict_
                                                      uint64_t* __restrict__ xr, uint32_t epoch, uint32_t spin,
                                                      float* __restrict__ part, uint16_t* __restrict__ Sop,
                                                      uint16_t* __restrict__ zop, uint32_t* __restrict__ gsg) {
-  // Partials of sub-block m are published in step m - L + 1, polled in step m - L + A and summed in step
-  // m - L + A + 1; r_k is polled in step m - 1 and used in step m.  With A = 2 every hop gets a full
-  // step between the store and the load that reads it.
-  constexpr int A = 2;
+  // Sub-block m: partials published early in step m - L + 1 (movers), polled early in step m - A - 1
+  // and summed in step m - A (leader), r_k published late in step m - A and polled early in step m - 1
+  // (consumer), used in step m.  Each wave checks the polls it issued a step earlier and issues the
+  // next ones right away, so every load has a full step to return; with L = 6, A = 3 every store also
+  // has at least a step before the load that reads it.
+  constexpr int A = 3;
   static_assert(L >= A + 3, "each hop of the exchange needs a full step");
   // The K ring, then V, r and the leader's partials; the ring is reused for the end-of-chunk combine.
   __shared__ __attribute__((aligned(16))) uint16_t Kr[L * kSB * kPitch];
@@ -143,7 +149,8 @@ __global__ __launch_bounds__(256, 2) void kv_state_x(const uint16_t* __restrict_
   float* fin = reinterpret_cast<float*>(Kr);
 
   const int p = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
-  const int P = (H + 1) / 2, C = H * kHeadDim;
+  const int P = (H + 1) / 2;
+  const float inv_C = 1.0f / (float)(H * kHeadDim);
   const int h0 = 2 * p;
   const int nh = min(2, H - h0);
   const int n_begin = c * Tc;
@@ -200,7 +207,8 @@ __global__ __launch_bounds__(256, 2) void kv_state_x(const uint16_t* __restrict_
   // q * (64 / G) + lane / G, partial lane % G; for P > 64 (one owned token at most), partial lane + 64 q.
   // At most 4 slots are ever needed.
   const int G = seg_lanes(P);
-  const int tpp = 64 / G;
+  const int lgG = __builtin_ctz(G);
+  const int tpp = 64 >> lgG;
   uint64_t lx0[4] = {0, 0, 0, 0};
   int ltok[4] = {0, 0, 0, 0}, lk[4] = {0, 0, 0, 0};
   bool lvalid[4] = {false, false, false, false};
@@ -213,8 +221,8 @@ __global__ __launch_bounds__(256, 2) void kv_state_x(const uint16_t* __restrict_
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(xpart + (row0 + lnm0) * P, (uint32_t)(mrows * P * 8));
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      ltok[q] = P <= 64 ? q * tpp + lane / G : 0;
-      lk[q] = P <= 64 ? lane % G : lane + 64 * q;
+      ltok[q] = P <= 64 ? q * tpp + (lane >> lgG) : 0;
+      lk[q] = P <= 64 ? lane & (G - 1) : lane + 64 * q;
       lvalid[q] = ltok[q] < lowned && lk[q] < P && (P <= 64 || q < 3);
       lx0[q] = buffer_get_tagged(rl, lvalid[q] ? (uint32_t)(((p + ltok[q] * P) * P + lk[q]) * 8) : kOutOfRange);
     }
@@ -228,7 +236,7 @@ __global__ __launch_bounds__(256, 2) void kv_state_x(const uint16_t* __restrict_
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(xr + row0 + n0, (uint32_t)(crows * 8));
     rx0 = buffer_get_tagged(rc, lane < crows ? (uint32_t)(lane * 8) : kOutOfRange);
   };
-  if (w == 1) leader_issue(-A);          // the first step's sub-block m (negative: no loads)
+  if (w == 1) leader_issue(-(L - 1) + A);  // the first step's sub-block m (negative: no loads)
   if (w == 0) consumer_issue(-(L - 1));  // likewise
   if (mover) load_rows(k, 0, pk);
   for (int j = -(L - 1); j < S; ++j) {
@@ -262,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void kv_state_x(const uint16_t* __restrict_
       }
     }
     // (2) Tokens p, p + P, ... of sub-block m: their P partials summed, r_k published.
-    const int m = j + L - 1 - A;
+    const int m = j + A;
     if (w == 1) {
       // Polls for sub-block m were issued in the previous step: check them and form r_k of the owned
       // tokens; then issue the polls for sub-block m + 1 (published a step ago), to be checked in the
@@ -273,11 +281,16 @@ __global__ __launch_bounds__(256, 2) void kv_state_x(const uint16_t* __restrict_
       const __amdgpu_buffer_rsrc_t rr = make_rsrc(xr + row0 + lnm0, in_m ? (uint32_t)(min(kSB, n_end - lnm0) * 8) : 0u);
       float rq[4] = {0.f, 0.f, 0.f, 0.f};
       uint32_t roff[4] = {kOutOfRange, kOutOfRange, kOutOfRange, kOutOfRange};
+      bool ready = false;
+      float val[4] = {0.f, 0.f, 0.f, 0.f};
+      const int owned_m = lowned;
+      int tok_m[4];
+      bool valid_m[4];
       if (in_m) {
         bool mine = true;
 #pragma unroll
         for (int q = 0; q < 4; ++q) mine = mine && (!lvalid[q] || tag_is(lx0[q], epoch));
-        bool ready = __all(mine);
+        ready = __all(mine);
         if (!ready) {
           const uint64_t t0 = now_ticks();
           while (now_ticks() - t0 <= spin) {
@@ -295,45 +308,57 @@ __global__ __launch_bounds__(256, 2) void kv_state_x(const uint16_t* __restrict_
             }
           }
         }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        val[q] = lvalid[q] ? tagged_value(lx0[q]) : 0.f;
+        tok_m[q] = ltok[q];
+        valid_m[q] = lvalid[q];
+      }
+      const int nm0 = lnm0;
+      leader_issue(m + 1);  // a full step before they are checked
+      if (in_m) {
         if (ready) {
           if (P <= 64) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              if (q * tpp >= lowned) break;  // uniform
-              const float x = seg_butterfly(lvalid[q] ? 0.f + tagged_value(lx0[q]) : 0.f, G);
-              rq[q] = r_from_ssq(x, C, eps);
-              if (lane % G == 0 && ltok[q] < lowned) roff[q] = (uint32_t)((p + ltok[q] * P) * 8);
+              if (q * tpp >= owned_m) break;  // uniform
+              const float x = seg_butterfly(valid_m[q] ? 0.f + val[q] : 0.f, G);
+              rq[q] = r_from_ssq(x, inv_C, eps);
+              if ((lane & (G - 1)) == 0 && tok_m[q] < owned_m) roff[q] = (uint32_t)((p + tok_m[q] * P) * 8);
             }
-          } else if (lowned > 0) {
+          } else if (owned_m > 0) {
             float a = 0.f;
 #pragma unroll
             for (int q = 0; q < 3; ++q)
-              if (lvalid[q]) a += tagged_value(lx0[q]);
-            rq[0] = r_from_ssq(seg_butterfly(a, 64), C, eps);
+              if (valid_m[q]) a += val[q];
+            rq[0] = r_from_ssq(seg_butterfly(a, 64), inv_C, eps);
             if (lane == 0) roff[0] = (uint32_t)(p * 8);
           }
         } else {
-          for (int i = 0; i < lowned; ++i) {  // a partial is late: the whole rows, same arithmetic
-            const int64_t row = row0 + lnm0 + p + i * P;
-            const float r = row_r<F16>(k + row * ld, H, P, eps, lane);
+          for (int i = 0; i < owned_m; ++i) {  // a partial is late: the whole rows, same arithmetic
+            const int64_t row = row0 + nm0 + p + i * P;
+            const float r = row_r<F16>(k + row * ld, H, P, inv_C, eps, lane);
             if (lane == 0) put_tagged(xr + row, r, epoch);
           }
         }
       }
-      leader_issue(m + 1);
 #pragma unroll
       for (int q = 0; q < 4; ++q) buffer_put_tagged(rr, roff[q], rq[q], epoch);
     }
     // (3) r_k of sub-block j (wave 0, one token per lane).
     if (w == 0) {
-      // The poll for sub-block j was issued in the previous step; the one for j + 1 goes out now.
+      // The poll for sub-block j was issued in the previous step; the one for j + 1 goes out as soon as
+      // this one has been read.
+      const uint64_t got = rx0;
+      consumer_issue(j + 1);
       if (j >= 0) {
         const int n0 = n_begin + j * kSB;
         const int crows = min(kSB, n_end - n0);
         float r = 1.0f;  // rows past the end hold zeros
         bool have = lane >= crows;
-        if (!have && tag_is(rx0, epoch)) {
-          r = tagged_value(rx0);
+        if (!have && tag_is(got, epoch)) {
+          r = tagged_value(got);
           have = true;
         }
         const uint64_t t0 = now_ticks();
@@ -349,14 +374,13 @@ __global__ __launch_bounds__(256, 2) void kv_state_x(const uint16_t* __restrict_
         const uint64_t late = __ballot(!have);
         if (lane == 0) missing = late;
       }
-      consumer_issue(j + 1);
     }
     __syncthreads();
     if (j >= 0 && missing != 0) {  // uniform: r_k of late tokens from their full rows
       const uint64_t late = missing;
       for (int t = w; t < kSB; t += 4)
         if ((late >> t) & 1) {
-          const float r = row_r<F16>(k + (row0 + n_begin + j * kSB + t) * ld, H, P, eps, lane);
+          const float r = row_r<F16>(k + (row0 + n_begin + j * kSB + t) * ld, H, P, inv_C, eps, lane);
           if (lane == 0) rs[t] = r;
         }
       __syncthreads();
@@ -443,7 +467,7 @@ hipError_t launch_kv_state_x(bool f16, const uint16_t* k, const uint16_t* v, int
                              const float* gk, int B, int N, int H, int Tc, int NC, float eps, void* xchg,
                              uint32_t epoch, uint32_t spin_ticks, float* part, uint16_t* Sop, uint16_t* zop,
                              uint32_t* gsg, hipStream_t stream) {
-  constexpr int L = 5;
+  constexpr int L = 6;
   const int P = (H + 1) / 2;
   uint64_t* xpart = static_cast<uint64_t*>(xchg);
   uint64_t* xr = xpart + (size_t)B * N * P;
