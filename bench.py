@@ -12,6 +12,10 @@ reduction and output: the whole path).
   python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload config4|config1|config2|config3|config5|w8a8|mixffn]
                   [--no-cold] [--no-secondary] [--no-cpu-baseline]
   python bench.py --mode copy        # plain device copy of known size (counter calibration under rocprofv3)
+  python bench.py --summarize-trace TRACE.db WORKLOAD OUT.txt COMMAND...
+                                     # rocprofv3 --kernel-trace database -> per-kernel summary under profiles/
+  python bench.py --summarize-counters WORKLOAD OUT.txt "COMMANDS" PMC.db...
+                                     # rocprofv3 --pmc databases -> per-kernel counter summary (MFMA busy, waits, ...)
   python bench.py --summarize-traffic KERNEL_FETCH.db KERNEL_WRITE.db COPY_FETCH.db COPY_WRITE.db
                                      # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE databases -> profiles/hbm_traffic.txt
 """
@@ -342,8 +346,8 @@ def summarize_traffic(kfetch: str, kwrite: str, cfetch: str, cwrite: str, worklo
              "# Counter KiB x 1024 x calibration; calibration = 268435456 / (counter bytes of a plain",
              "# device copy of 268435456 bytes, bench.py --mode copy).",
              "# Commands (from /tmp, TMPDIR=/tmp, one pass each):",
-             "#   rocprofv3 --pmc FETCH_SIZE -d kfetch -o run -- python3 /root/repo/bench.py --steps 3 --warmup 1 "
-             "--no-cpu-baseline --no-secondary",
+             "#   rocprofv3 --pmc FETCH_SIZE -d kfetch -o run -- python3 /root/repo/bench.py --steps 2 --warmup 1 "
+             "--no-cpu-baseline --no-secondary --no-cold --workload config4",
              "#   rocprofv3 --pmc WRITE_SIZE -d kwrite -o run -- (same bench command)",
              "#   rocprofv3 --pmc FETCH_SIZE -d cfetch -o run -- python3 /root/repo/bench.py --mode copy",
              "#   rocprofv3 --pmc WRITE_SIZE -d cwrite -o run -- python3 /root/repo/bench.py --mode copy",
@@ -365,7 +369,92 @@ def summarize_traffic(kfetch: str, kwrite: str, cfetch: str, cwrite: str, worklo
     return "\n".join(lines) + "\n"
 
 
+def summarize_trace(db: str, workload: str, command: str) -> str:
+    """Per-kernel duration statistics of a rocprofv3 --kernel-trace database (its `kernels` view)."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, duration from kernels").fetchall()
+    acc = {}
+    for name, dur in rows:
+        acc.setdefault(name, []).append(float(dur) / 1000.0)  # ns -> us
+    total = sum(sum(v) for v in acc.values())
+
+    def short(name: str) -> str:
+        n = name.split("(")[0]
+        return n.replace("void ", "").replace("sanala::", "").replace("at::native::", "torch ")
+
+    lines = [f"# rocprofv3 kernel-trace summary: {WORKLOADS[workload]['desc']}",
+             f"# Command (from /tmp, TMPDIR=/tmp): {command}",
+             f"# source_hash {source_hash()}",
+             "# Calls include warm-up and the per-kernel event-timed repetitions of bench.py.",
+             "#",
+             f"# {'kernel':58s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'share%':>7s}"]
+    for name, v in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"  {short(name)[:58]:58s} {len(v):6d} {sum(v) / len(v):9.2f} {min(v):9.2f} {max(v):9.2f} "
+                     f"{100.0 * sum(v) / total:7.2f}")
+    return "\n".join(lines) + "\n"
+
+
+def summarize_counters(dbs, workload: str, command: str) -> str:
+    """Per-kernel means of the counters in rocprofv3 --pmc databases (one pass each), with derived
+    figures: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE of one XCD x 1024 SIMDs); waves waiting to
+    issue = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES, waiting on anything = SQ_WAIT_ANY / SQ_WAVE_CYCLES; LDS
+    bank conflicts per LDS-active cycle; L2 hit rate = TCC_HIT / (TCC_HIT + TCC_MISS)."""
+    import sqlite3
+    per = {}
+    for db in dbs:
+        con = sqlite3.connect(db)
+        rows = con.execute("select kernel_name, counter_name, value from counters_collection").fetchall()
+        for name, ctr, val in rows:
+            per.setdefault(name, {}).setdefault(ctr, []).append(float(val))
+    lines = [f"# rocprofv3 counter summary: {WORKLOADS[workload]['desc']}",
+             f"# Commands (from /tmp, TMPDIR=/tmp), one counter pass each: {command}",
+             f"# source_hash {source_hash()}",
+             "# Values are means per dispatch (GRBM_GUI_ACTIVE as stored: summed over the 8 XCDs).  Derived:",
+             "# mfma_busy% = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs); wait_issue% =",
+             "# SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; wait_any% = SQ_WAIT_ANY / SQ_WAVE_CYCLES;",
+             "# lds_conflict% = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; l2_hit% = TCC_HIT / (TCC_HIT + TCC_MISS)."]
+    for name, ctrs in sorted(per.items()):
+        if "sanala" not in name:
+            continue
+        m = {c: sum(v) / len(v) for c, v in ctrs.items()}
+        short = name.split("(")[0].replace("void ", "").replace("sanala::", "")
+        lines.append(f"kernel: {short}")
+        for c in sorted(m):
+            lines.append(f"  {c}: {m[c]:.6g}")
+        g = m.get("GRBM_GUI_ACTIVE")
+        if g and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            # the database holds GRBM_GUI_ACTIVE summed over the 8 XCDs; the busy-cycle ratio wants one XCD's
+            lines.append(f"  gpu_active_cycles_per_xcd: {g / 8:.6g}")
+            lines.append(f"  mfma_busy%: {100.0 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (g / 8 * 1024):.1f}")
+        if m.get("SQ_WAVE_CYCLES"):
+            if "SQ_WAIT_INST_ANY" in m:
+                lines.append(f"  wait_issue%: {100.0 * m['SQ_WAIT_INST_ANY'] / m['SQ_WAVE_CYCLES']:.1f}")
+            if "SQ_WAIT_ANY" in m:
+                lines.append(f"  wait_any%: {100.0 * m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.1f}")
+        if m.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in m:
+            lines.append(f"  lds_conflict%: {100.0 * m['SQ_LDS_BANK_CONFLICT'] / m['SQ_LDS_IDX_ACTIVE']:.2f}")
+        hit, miss = m.get("TCC_HIT_sum", m.get("TCC_HIT")), m.get("TCC_MISS_sum", m.get("TCC_MISS"))
+        if hit is not None and miss is not None and hit + miss > 0:
+            lines.append(f"  l2_hit%: {100.0 * hit / (hit + miss):.1f}")
+    return "\n".join(lines) + "\n"
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
+        # --summarize-counters WORKLOAD OUTFILE "COMMAND" DB...
+        text = summarize_counters(sys.argv[5:], sys.argv[2], sys.argv[4])
+        with open(sys.argv[3], "w") as f:
+            f.write(text)
+        print(text)
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
+        # --summarize-trace DB WORKLOAD OUTFILE COMMAND...
+        text = summarize_trace(sys.argv[2], sys.argv[3], " ".join(sys.argv[5:]))
+        with open(sys.argv[4], "w") as f:
+            f.write(text)
+        print(text)
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-traffic":
         text = summarize_traffic(*sys.argv[2:6])
         with open(os.path.join(ROOT, "profiles", "hbm_traffic.txt"), "w") as f:

@@ -111,6 +111,11 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int C, int8_t* xq, fl
 // false when timing is off.
 bool timing_slot(const char* name, hipEvent_t* begin, hipEvent_t* end);
 
+// The event the kernels of the current call on this host thread signal when they complete (the scratch
+// buffer's last use), or nullptr.  launch_kernel attaches it to every launch as the dispatch's stop
+// event, so the last kernel's completion sets it without an extra marker packet in the queue.
+hipEvent_t& stop_event();
+
 // Raises `kernel`'s dynamic-LDS limit to `bytes` on the current device, once per (kernel, device);
 // safe to call from several host threads.
 hipError_t ensure_max_lds(const void* kernel, int bytes);
@@ -124,6 +129,8 @@ inline void launch_kernel(const char* name, void (*kernel)(P...), dim3 grid, dim
   hipEvent_t b = nullptr, e = nullptr;
   if (timing_slot(name, &b, &e))
     hipExtLaunchKernelGGL(kernel, grid, block, (std::uint32_t)lds, stream, b, e, 0u, args...);
+  else if (hipEvent_t se = stop_event())
+    hipExtLaunchKernelGGL(kernel, grid, block, (std::uint32_t)lds, stream, nullptr, se, 0u, args...);
   else
     kernel<<<grid, block, lds, stream>>>(args...);
 }

@@ -55,11 +55,38 @@ struct HipBackend {
 HipBackend g_backend;
 sanala::ScratchTable<HipBackend> g_table(g_backend);
 
+// Per-host-thread kernel timing (measurement support).
+struct TimedKernel {
+  const char* name;
+  hipEvent_t begin, end;
+};
+struct Timing {
+  bool enabled = false;
+  int count = 0;
+  std::vector<TimedKernel> slots;
+  ~Timing() {
+    for (auto& t : slots) {
+      (void)hipEventDestroy(t.begin);
+      (void)hipEventDestroy(t.end);
+    }
+  }
+};
+thread_local Timing g_timing;
+
+// A call's hold on its stream's scratch.  While held, the kernels of the call carry the buffer's
+// last-use event as their stop event (launch_kernel); with kernel timing on they carry the timing
+// events instead, and the last-use event is recorded when the lease ends.
 class ScratchLease {
  public:
   hipError_t acquire(int dev, hipStream_t stream, size_t bytes) {
-    return g_table.acquire(lease_, dev, stream, bytes) == 0 ? hipSuccess : hipErrorOutOfMemory;
+    if (g_table.acquire(lease_, dev, stream, bytes) != 0) return hipErrorOutOfMemory;
+    if (!g_timing.enabled) {
+      sanala::stop_event() = static_cast<hipEvent_t>(lease_.event());
+      lease_.attached();
+    }
+    return hipSuccess;
   }
+  ~ScratchLease() { sanala::stop_event() = nullptr; }
   void* ptr() const { return lease_.ptr(); }
 
  private:
@@ -112,23 +139,6 @@ sana_status_t check_common(int B, int N, int H, int D, float eps, const float* g
   return SANA_OK;
 }
 
-// Per-host-thread kernel timing (measurement support).
-struct TimedKernel {
-  const char* name;
-  hipEvent_t begin, end;
-};
-struct Timing {
-  bool enabled = false;
-  int count = 0;
-  std::vector<TimedKernel> slots;
-  ~Timing() {
-    for (auto& t : slots) {
-      (void)hipEventDestroy(t.begin);
-      (void)hipEventDestroy(t.end);
-    }
-  }
-};
-thread_local Timing g_timing;
 
 }  // namespace
 
@@ -145,6 +155,11 @@ hipError_t ensure_max_lds(const void* kernel, int bytes) {
   e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e == hipSuccess) done.emplace_back(kernel, dev);
   return e;
+}
+
+hipEvent_t& stop_event() {
+  thread_local hipEvent_t ev = nullptr;
+  return ev;
 }
 
 bool timing_slot(const char* name, hipEvent_t* begin, hipEvent_t* end) {

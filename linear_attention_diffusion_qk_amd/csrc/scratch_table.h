@@ -8,9 +8,10 @@
 //    buffer stream-ordered on s and takes a larger one.
 //  * The table grows with the number of streams in use; there is no fixed cap.
 //  * A stream handle can be reused by the runtime for a new stream once the old one is destroyed, while
-//    work the old stream queued may still be running on the old stream's buffer.  Each call records an
-//    event on its stream after its work (the buffer's last use); the next call on the entry makes its
-//    stream wait for that event unless it has already completed.  On the same stream that wait is
+//    work the old stream queued may still be running on the old stream's buffer.  Each call's work
+//    signals an event when it completes (the buffer's last use: the kernels carry it as their stop
+//    event, or it is recorded after them); the next call on the entry makes its stream wait for that
+//    event unless it has already completed.  On the same stream that wait is
 //    implied by stream order anyway; on a new stream behind a reused handle it is what keeps the old
 //    kernels and the new ones apart.
 //  * release(dev, s) frees s's buffer stream-ordered on s (so s must still exist) and empties the entry
@@ -57,16 +58,21 @@ class ScratchTable {
     ~Lease() {
       if (!e_) return;
       // The buffer's last use: everything the caller enqueued on the stream while holding the lease.
-      e_->recorded = t_->be_.event_record(e_->last_use, e_->stream) == 0;
+      // Either the caller's work signalled the event itself (attached), or it is recorded here.
+      e_->recorded = attached_ || t_->be_.event_record(e_->last_use, e_->stream) == 0;
       e_->mu.unlock();
     }
     void* ptr() const { return e_ ? e_->ptr : nullptr; }
     size_t bytes() const { return e_ ? e_->bytes : 0; }
+    // The last-use event, for work that signals it on completion (then call attached()).
+    void* event() const { return e_ ? e_->last_use : nullptr; }
+    void attached() { attached_ = true; }
 
    private:
     friend class ScratchTable;
     Entry* e_ = nullptr;
     ScratchTable* t_ = nullptr;
+    bool attached_ = false;
   };
 
   enum Result { kOk = 0, kErrAlloc = 1, kErrFree = 2, kErrSync = 3 };

@@ -17,7 +17,7 @@ struct Fake {
   std::map<void*, void*> recorded_on;          // event -> stream of its last record
   std::map<void*, bool> done;                  // event -> completed
   std::vector<std::pair<void*, void*>> waits;  // (stream, event)
-  int allocs = 0, events = 0;
+  int allocs = 0, events = 0, records = 0;
   int alloc_async(void** p, size_t bytes, void*) {
     std::lock_guard<std::mutex> lk(mu);
     *p = std::malloc(1);
@@ -42,6 +42,7 @@ struct Fake {
     std::lock_guard<std::mutex> lk(mu);
     recorded_on[ev] = s;
     done[ev] = false;  // work queued behind it is still running
+    ++records;
     return 0;
   }
   int event_done(void* ev) {
@@ -128,6 +129,26 @@ int main() {
       CHECK(t.acquire(l, 0, S(9), 64) == Table::kOk);
       CHECK(be.waits.size() == w0 + 1 && l.ptr() == bufs[9]);
     }
+  }
+  // 4b. Work that signals the event itself (attached): no separate record, and the next acquire still
+  // waits for it while it is pending.
+  {
+    be.complete_all();
+    void* ev = nullptr;
+    const int records = be.records;
+    {
+      Table::Lease l;
+      CHECK(t.acquire(l, 0, S(13), 64) == Table::kOk);
+      ev = l.event();
+      CHECK(ev != nullptr);
+      l.attached();
+      be.done[ev] = false;  // the call's kernels, carrying the event, are still running
+    }
+    CHECK(be.records == records);  // no separate record for an attached lease
+    const size_t w0 = be.waits.size();
+    Table::Lease l;
+    CHECK(t.acquire(l, 0, S(13), 64) == Table::kOk);
+    CHECK(be.waits.size() == w0 + 1 && be.waits.back().second == ev);
   }
   // 5. Release frees on the stream and empties the entry; a new stream reuses the slot.
   {
