@@ -128,7 +128,7 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
   size_t off = 0;
   p.off_rk = off;   off = align_up(off + (norm ? (size_t)B * N * 4 : 0), 256);
   p.off_rq = off;
-  off = align_up(off + (norm && bf && (H > 72 || p.out_kind == kOutTileGroups) ? (size_t)B * N * 4 : 0), 256);
+  off = align_up(off + (norm && (!bf || H > 72 || p.out_kind == kOutTileGroups) ? (size_t)B * N * 4 : 0), 256);
   p.off_part = off; off = align_up(off + (p.NC > 1 || !bf ? BH * p.NC * kPartStrideBytes : 0), 256);
   p.off_S32 = off;  off = align_up(off + (bf ? 0 : BH * kHeadDim * kHeadDim * 4), 256);
   p.off_z = off;    off = align_up(off + (bf ? 0 : BH * kHeadDim * 4), 256);
