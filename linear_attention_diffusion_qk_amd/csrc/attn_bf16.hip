@@ -34,28 +34,24 @@
 namespace sanala {
 
 // ---------------------------------------------------------------------------------------------
-// KV state.  Block = 4 waves; block (c, p, b) owns heads 2p, 2p+1 and tokens [c*Tc, min(N, c*Tc+Tc)),
-// staged through LDS in 64-token sub-blocks; the next sub-block's global loads are in flight while
-// the current one is multiplied.  Wave w: head 2p + (w & 1), token half (w >> 1) of each sub-block.
-// MFMA 32x32x16: A[d][t] = bf16(r_t ReLU(s_d k_t,d)) (lane d + 32g holds tokens 8g..8g+7 of the
-// 16-token step), B[t][e] = v_t,e; accumulator lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4,
-// column l%32.  A second MFMA against an all-ones B gives z~ in every column.
+// KV state of one chunk.  The block (4 waves) forms the state of heads 2p, 2p+1 over tokens
+// [c*Tc, min(N, c*Tc+Tc)) of sample b, staged through LDS in 64-token sub-blocks; the next
+// sub-block's global loads are in flight while the current one is multiplied.  Wave w: head 2p + (w & 1),
+// token half (w >> 1) of each sub-block.  MFMA 32x32x16: A[d][t] = bf16(r_t ReLU(s_d k_t,d)) (lane
+// d + 32g holds tokens 8g..8g+7 of the 16-token step), B[t][e] = v_t,e; accumulator lane l, register
+// r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32.  A second MFMA against an all-ones B gives z~ in
+// every column.  On return (after a barrier) fin holds, per head, S~[d][e] then z~[d] (kPartStride
+// floats), the two token halves added in a fixed order.
 // ---------------------------------------------------------------------------------------------
-template <bool NORM, bool F16>
-__global__ __launch_bounds__(256, 5) void kv_state_bf16(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                                                     int64_t ld, const float* __restrict__ r_k,
-                                                     const float* __restrict__ gq, const float* __restrict__ gk,
-                                                     int N, int H, int Tc, int NC, float* __restrict__ part,
-                                                     uint16_t* __restrict__ Sop, uint16_t* __restrict__ zop,
-                                                     uint32_t* __restrict__ gsg) {
-  constexpr int SB = 64;     // tokens per sub-block
-  constexpr int PITCH = 72;  // bf16 per staged row (64 used)
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[SB * PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[SB * PITCH];
-  __shared__ __attribute__((aligned(16))) float rs[SB];
-  __shared__ float fin[2 * kPartStride];  // wave hand-over, then the block's state of the head pair
+constexpr int kStateSB = 64;     // tokens per sub-block
+constexpr int kStatePitch = 72;  // bf16 per staged row (64 used)
 
-  const int c = blockIdx.x, p = blockIdx.y, b = blockIdx.z;
+template <bool NORM, bool F16>
+__device__ __forceinline__ void chunk_state(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t ld,
+                                            const float* __restrict__ r_k, const float* __restrict__ gk, int N, int H,
+                                            int b, int p, int c, int Tc, uint16_t* Ks, uint16_t* Vs, float* rs,
+                                            float* fin) {
+  constexpr int SB = kStateSB, PITCH = kStatePitch;
   const int h0 = 2 * p;
   const int nh = min(2, H - h0);
   const int n_begin = c * Tc;
@@ -140,8 +136,7 @@ __global__ __launch_bounds__(256, 5) void kv_state_bf16(const uint16_t* __restri
     __syncthreads();
   }
 
-  // Combine the two token halves of each head in a fixed order (wave hh + 2 hands over to wave hh),
-  // leaving the block's state of head hh as S~[d][e] and z~[d] in `fin`.
+  // Combine the two token halves of each head in a fixed order (wave hh + 2 hands over to wave hh).
   float* fh = fin + hh * kPartStride;
   if (th == 1) {
 #pragma unroll
@@ -161,22 +156,170 @@ __global__ __launch_bounds__(256, 5) void kv_state_bf16(const uint16_t* __restri
     }
   }
   __syncthreads();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Chunk rendezvous (a split sequence whose state blocks are all resident at once).  Block (c, p, b)
+// stores its chunk partial with device-scope stores, waits for them to complete and sets its flag to
+// the call's tag; it then waits, up to a time limit, for the flags of the pair's other chunks, and sums
+// slice c of the pair's state over all chunks in chunk order (one round of loads), writing that slice
+// of the output kernel's operands.  So the NC blocks of a pair share the reduction that would otherwise
+// be a launch of its own.  A chunk whose flag has not appeared by the limit (its block not resident
+// yet, say) is formed by the waiting block itself with the same code, so the bits do not depend on the
+// route and no wait can hang.  The flags carry the call's tag (never 0), so they need no clearing.
+// No fence is used: an agent-scope fence writes back and invalidates the whole L2 of the XCD, which
+// made the state pass six times slower on MI355X while other blocks streamed K and V through that L2.
+// ---------------------------------------------------------------------------------------------
+constexpr int kMaxRendezvousChunks = 16;
+
+// Stores the block's partial of heads h0 .. h0+nh-1 (fin: kPartStride floats per head) as chunk c of
+// NC, device-scope 16-byte stores; then, once every thread's stores have completed, sets the flag.
+__device__ __forceinline__ void publish_partial(float* __restrict__ part, const float* fin, int NC, int c, int64_t bh0,
+                                                int nh, uint32_t* flag, uint32_t epoch) {
+  constexpr int Q4 = kPartStride / 4;
+  for (int hl = 0; hl < nh; ++hl) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(part + ((bh0 + hl) * NC + c) * kPartStride, kPartStride * 4);
+    for (int j = threadIdx.x; j < Q4; j += blockDim.x)
+      buffer_store16_dev(r, (uint32_t)(j * 16), *reinterpret_cast<const u32x4*>(fin + hl * kPartStride + 4 * j));
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wave 0 polls the NC (<= 64) flags until all carry the tag or `spin` ticks of the 100 MHz clock have
+// passed; every thread gets the mask of chunks still missing.
+__device__ __forceinline__ uint64_t wait_flags(const uint32_t* flags, int NC, uint32_t epoch, uint32_t spin) {
+  __shared__ uint64_t missing_s;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const uint64_t want = NC >= 64 ? ~0ull : ((1ull << NC) - 1ull);
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    uint64_t ready;
+    for (;;) {
+      const uint32_t f =
+          lane < NC ? __hip_atomic_load(const_cast<uint32_t*>(flags) + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                    : 0u;
+      ready = __ballot(f == epoch) & want;
+      if (ready == want || __builtin_amdgcn_s_memrealtime() - t0 >= spin) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (lane == 0) missing_s = want & ~ready;
+  }
+  __syncthreads();
+  return missing_s;
+}
+
+// Slice c of the pair's summed state (16-byte column groups [c*per, (c+1)*per) of the nh*kPartStride
+// floats), summed over the NC chunks in chunk order, then written as operands.  Chunks in `missing` are
+// formed here (chunk_state into fin) instead of being loaded.
+template <bool NORM, bool F16>
+__device__ __forceinline__ void reduce_slice(const float* __restrict__ part, uint64_t missing, int NC, int c, int64_t bh0,
+                                             int h0, int nh, const uint16_t* __restrict__ k,
+                                             const uint16_t* __restrict__ v, int64_t ld, const float* __restrict__ r_k,
+                                             const float* __restrict__ gq, const float* __restrict__ gk, int N, int H,
+                                             int b, int p, int Tc, uint16_t* Ks, uint16_t* Vs, float* rs, float* fin,
+                                             f32x4* accs, uint16_t* __restrict__ Sop, uint16_t* __restrict__ zop) {
+  constexpr int Q4 = kPartStride / 4;
+  const int cols = nh * Q4;
+  const int per = (cols + NC - 1) / NC;
+  const int j0 = c * per, j1 = min(cols, j0 + per);
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(part + bh0 * NC * kPartStride, (uint32_t)(nh * NC * kPartStride * 4));
+  auto emit4 = [&](int j, f32x4 s) {
+    const int hl = j / Q4, off = 4 * (j - hl * Q4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) emit_state<NORM>(bh0 + hl, h0 + hl, off + e, s[e], gq, gk, Sop, zop);
+  };
+  auto src_off = [&](int j, int u) {  // byte offset of column group j of chunk u
+    const int hl = j / Q4;
+    return (uint32_t)(((hl * NC + u) * kPartStride + 4 * (j - hl * Q4)) * 4);
+  };
+  if (missing == 0) {
+    for (int j = j0 + (int)threadIdx.x; j < j1; j += blockDim.x) {
+      f32x4 x[kMaxRendezvousChunks];
+#pragma unroll
+      for (int u = 0; u < kMaxRendezvousChunks; ++u)
+        x[u] = as_f32x4(buffer_load16_dev(r, u < NC ? src_off(j, u) : kOutOfRange));
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < kMaxRendezvousChunks; ++u)
+        if (u < NC) {
+          s[0] += x[u][0];
+          s[1] += x[u][1];
+          s[2] += x[u][2];
+          s[3] += x[u][3];
+        }
+      emit4(j, s);
+    }
+    return;
+  }
+  // Some partial is missing: the same sums, chunk by chunk, accumulated in LDS (each thread its own
+  // column groups), with the missing chunks formed by this block.
+  for (int j = j0 + (int)threadIdx.x; j < j1; j += blockDim.x) accs[j - j0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < NC; ++u) {
+    if ((missing >> u) & 1ull) {
+      chunk_state<NORM, F16>(k, v, ld, r_k, gk, N, H, b, p, u, Tc, Ks, Vs, rs, fin);
+      for (int j = j0 + (int)threadIdx.x; j < j1; j += blockDim.x) {
+        const int hl = j / Q4;
+        accs[j - j0] += *reinterpret_cast<const f32x4*>(fin + hl * kPartStride + 4 * (j - hl * Q4));
+      }
+      __syncthreads();  // fin is reused by the next chunk formed here
+    } else {
+      for (int j = j0 + (int)threadIdx.x; j < j1; j += blockDim.x)
+        accs[j - j0] += as_f32x4(buffer_load16_dev(r, src_off(j, u)));
+    }
+  }
+  for (int j = j0 + (int)threadIdx.x; j < j1; j += blockDim.x) emit4(j, accs[j - j0]);
+}
+
+// ---------------------------------------------------------------------------------------------
+// KV state pass.  Block (c, p, b): chunk c of heads 2p, 2p+1 of sample b (chunk_state).  One chunk per
+// sequence: the block writes the operands itself.  Several: with flags set, the chunk rendezvous above;
+// otherwise the block writes its partial for kv_reduce_bf16.
+// ---------------------------------------------------------------------------------------------
+template <bool NORM, bool F16>
+__global__ __launch_bounds__(256, 5) void kv_state_bf16(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                     int64_t ld, const float* __restrict__ r_k,
+                                                     const float* __restrict__ gq, const float* __restrict__ gk,
+                                                     int N, int H, int Tc, int NC, float* __restrict__ part,
+                                                     uint16_t* __restrict__ Sop, uint16_t* __restrict__ zop,
+                                                     uint32_t* __restrict__ gsg, uint32_t* __restrict__ flags,
+                                                     uint32_t epoch, uint32_t spin) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kStateSB * kStatePitch];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[kStateSB * kStatePitch];
+  __shared__ __attribute__((aligned(16))) float rs[kStateSB];
+  __shared__ __attribute__((aligned(16))) float fin[2 * kPartStride];  // wave hand-over, then the block's state
+
+  const int c = blockIdx.x, p = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  chunk_state<NORM, F16>(k, v, ld, r_k, gk, N, H, b, p, c, Tc, Ks, Vs, rs, fin);
+  const int h0 = 2 * p;
+  const int nh = min(2, H - h0);
   const int64_t bh0 = (int64_t)b * H + h0;
+  if ((NC == 1 || (flags != nullptr && c == 0)) && b == 0 && tid < nh * kSgnPerHead) {
+    const int h = h0 + tid / kSgnPerHead, i = tid % kSgnPerHead;
+    gsg[h * kSgnPerHead + i] = sign_word<NORM>(gq, h, i / 4, i & 3);
+  }
   if (NC == 1) {
     for (int i = tid; i < nh * kPartStride; i += 256) {
       const int hl = i / kPartStride, off = i - hl * kPartStride;
       emit_state<NORM>(bh0 + hl, h0 + hl, off, fin[i], gq, gk, Sop, zop);
     }
-    if (b == 0 && tid < nh * kSgnPerHead) {
-      const int h = h0 + tid / kSgnPerHead, i = tid % kSgnPerHead;
-      gsg[h * kSgnPerHead + i] = sign_word<NORM>(gq, h, i / 4, i & 3);
+    return;
+  }
+  if (flags == nullptr) {
+    for (int i = tid; i < nh * kPartStride; i += 256) {
+      const int hl = i / kPartStride, off = i - hl * kPartStride;
+      part[((bh0 + hl) * NC + c) * kPartStride + off] = fin[i];
     }
     return;
   }
-  for (int i = tid; i < nh * kPartStride; i += 256) {
-    const int hl = i / kPartStride, off = i - hl * kPartStride;
-    part[((bh0 + hl) * NC + c) * kPartStride + off] = fin[i];
-  }
+  __shared__ f32x4 accs[(2 * kPartStride / 4 + 1) / 2];  // slow route of the rendezvous (NC >= 2)
+  uint32_t* pf = flags + ((int64_t)b * gridDim.y + p) * NC;
+  publish_partial(part, fin, NC, c, bh0, nh, pf + c, epoch);
+  const uint64_t missing = wait_flags(pf, NC, epoch, spin);
+  reduce_slice<NORM, F16>(part, missing, NC, c, bh0, h0, nh, k, v, ld, r_k, gq, gk, N, H, b, p, Tc, Ks, Vs, rs, fin,
+                          accs, Sop, zop);
 }
 
 // r[row] = 1 / sqrt(sum_j part[row * nparts + j] / C + eps): the QK-Norm scale from per-row partial
@@ -593,14 +736,18 @@ static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t l
     launch_kernel("rowstats_k", rowstats_kernel<uint16_t, F16>, rs_blocks, 256, 0, stream, k, ldkv, rows, C, eps, r_k,
                   nullptr, 0, nullptr);
   const dim3 grid(p.NC, (H + 1) / 2, B);
+  // Several chunks: reduced by the state blocks themselves (rendezvous) or by kv_reduce_bf16.
+  const bool rdv = p.rendezvous && !xchg;
+  uint32_t* flags = rdv ? reinterpret_cast<uint32_t*>(base + p.off_flags) : nullptr;
+  const uint32_t epoch = rdv ? next_epoch() : 0u;
   if (xchg) {
   } else if (p.norm)
     launch_kernel("kv_state", kv_state_bf16<true, F16>, grid, 256, 0, stream, k, v, ldkv, r_k, gq, gk, N, H, p.Tc, p.NC,
-                  part, Sop, zop, gsg);
+                  part, Sop, zop, gsg, flags, epoch, p.xchg_spin);
   else
     launch_kernel("kv_state", kv_state_bf16<false, F16>, grid, 256, 0, stream, k, v, ldkv, nullptr, nullptr, nullptr, N,
-                  H, p.Tc, p.NC, part, Sop, zop, gsg);
-  if (p.NC > 1) {
+                  H, p.Tc, p.NC, part, Sop, zop, gsg, flags, epoch, p.xchg_spin);
+  if (p.NC > 1 && !rdv) {
     const unsigned blocks = (unsigned)((BH * kPartStride + 255) / 256);
     if (p.norm)
       launch_kernel("kv_reduce", kv_reduce_bf16<true>, blocks, 256, 0, stream, part, p.NC, H, BH, gq, gk, Sop, zop,
@@ -624,6 +771,7 @@ static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t l
         p.norm ? ensure_max_lds(reinterpret_cast<const void*>(&out_persist_bf16<kPersistPPW, true, F16>), 160 * 1024)
                : ensure_max_lds(reinterpret_cast<const void*>(&out_persist_bf16<kPersistPPW, false, F16>), 160 * 1024);
     if (ea != hipSuccess) return ea;
+    final_launch();
     if (p.norm)
       launch_kernel("out", out_persist_bf16<kPersistPPW, true, F16>, nblk, nw * 64, lds, stream, q, ldq, gsg, Sop, zop,
                     B, N, H, eps, inv_C, out, ldo, per_arg);
@@ -635,6 +783,7 @@ static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t l
   if (groups) {
     constexpr int HPWG = 2;  // 8 heads per block (20 per block: 1024-token call 17.6 against 16.8 us)
     const dim3 ogrid((N + 15) / 16, B, (H + 4 * HPWG - 1) / (4 * HPWG));
+    final_launch();
     if (p.norm)
       launch_kernel("out", out_bf16<HPWG, true, true, F16>, ogrid, 256, 0, stream, q, ldq, gsg, Sop, zop, r_q, N, H,
                     eps, inv_C, out, ldo);
@@ -646,6 +795,7 @@ static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t l
   constexpr int HPW = 18;
   if (H <= 4 * HPW) {
     const dim3 ogrid((N + 15) / 16, B, 1);
+    final_launch();
     if (p.norm)
       launch_kernel("out", out_bf16<HPW, true, false, F16>, ogrid, 256, 0, stream, q, ldq, gsg, Sop, zop, nullptr, N, H,
                     eps, inv_C, out, ldo);
@@ -657,9 +807,11 @@ static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t l
     if (p.norm) {
       launch_kernel("rowstats_q", rowstats_kernel<uint16_t, F16>, rs_blocks, 256, 0, stream, q, ldq, rows, C, eps, r_q,
                     nullptr, 0, nullptr);
+      final_launch();
       launch_kernel("out", out_bf16<HPW, true, true, F16>, ogrid, 256, 0, stream, q, ldq, gsg, Sop, zop, r_q, N, H, eps,
                     inv_C, out, ldo);
     } else {
+      final_launch();
       launch_kernel("out", out_bf16<HPW, false, true, F16>, ogrid, 256, 0, stream, q, ldq, gsg, Sop, zop, nullptr, N, H,
                     eps, inv_C, out, ldo);
     }

@@ -225,6 +225,7 @@ hipError_t launch_attn_f32(const AttnPlan& p, const float* q, int64_t ldq, const
                   (int64_t)B * H, S32, z);
   }
   const dim3 ogrid((N + 15) / 16, B, (H + kF32OutHeads - 1) / kF32OutHeads);
+  final_launch();
   if (p.norm)
     launch_kernel("out", out_f32<true>, ogrid, 256, 0, stream, q, ldq, gq, r_q, S32, z, N, H, eps, out, ldo);
   else

@@ -36,7 +36,7 @@ uint32_t next_epoch() {
   uint32_t e = counter.fetch_add(1) + 1;
   while (e == 0) e = counter.fetch_add(1) + 1;  // 0 is what fresh memory holds
   return e;
-}  // the fp32 output kernel stages 4 rows of C floats in LDS
+}
 
 AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
   AttnPlan p{};
@@ -81,6 +81,7 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
     Tc = std::max(Tc, std::min(256, n64));
   }
   Tc = env_int("SANA_KV_CHUNK", Tc);
+  Tc = std::max(Tc, (N + 65535) / 65536);  // at most 65536 chunks: partial offsets stay within 32 bits
   Tc = std::max(64, (Tc + 63) / 64 * 64);
   p.Tc = Tc;
   p.NC = (N + Tc - 1) / Tc;
@@ -111,13 +112,24 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
   }
   // K row statistics inside the state pass (one read of K), for calls whose output kernel forms r_q
   // itself: SANA_STATE_XCHG=1 asks for it (off by default: on MI355X it measures slower than the
-  // separate row-statistics pass followed by the plain state pass).  SANA_XCHG_SPIN_US: the exchange's
-  // wait limit in microseconds (default 200; 0 makes every wait that is not met at once take the
-  // local route, which gives the same bits).
+  // separate row-statistics pass followed by the plain state pass).  SANA_XCHG_SPIN_US: the wait limit
+  // of the cross-block waits (this exchange and the chunk rendezvous) in microseconds (default 200; 0
+  // makes every wait that is not met at once take the local route, which gives the same bits).
   {
     const char* s = std::getenv("SANA_STATE_XCHG");
     const bool on = s && s[0] == '1' && s[1] == 0;
     p.state_xchg = bf && norm && p.out_kind != kOutTileGroups && on;
+  }
+  // A split sequence (16-bit path) is reduced by a launch of its own (kv_reduce).  SANA_STATE_RENDEZVOUS=1
+  // asks the state blocks to reduce the chunk partials among themselves instead, where every block of
+  // the grid can be resident at once (five per CU) and there are at most 16 chunks.  The two routes sum
+  // in the same order and give the same bits; on MI355X the rendezvous saves the launch but its tail
+  // costs as much (4K workload 68.5 against 68.2 us per call, 1024 tokens 18.7 against 18.3 us), so it
+  // is off by default.
+  {
+    const char* s = std::getenv("SANA_STATE_RENDEZVOUS");
+    const bool on = s && s[0] == '1' && s[1] == 0;
+    p.rendezvous = bf && p.NC > 1 && p.NC <= 16 && (int64_t)B * groups * p.NC <= 5 * (int64_t)p.num_cus && on;
   }
   {
     const char* s = std::getenv("SANA_XCHG_SPIN_US");
@@ -134,6 +146,8 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
   p.off_z = off;    off = align_up(off + (bf ? 0 : BH * kHeadDim * 4), 256);
   p.off_Sop = off;  off = align_up(off + (bf ? bf16_operand_bytes((int64_t)BH, H) : 0), 256);
   p.off_xchg = off; off = align_up(off + (p.state_xchg ? kv_state_x_exchange_bytes((int64_t)B * N, H) : 0), 256);
+  // Rendezvous flags, one word per (sample, head pair, chunk).
+  p.off_flags = off; off = align_up(off + (p.rendezvous ? (size_t)B * groups * p.NC * 4 : 0), 256);
   p.ws_bytes = off;
   return p;
 }

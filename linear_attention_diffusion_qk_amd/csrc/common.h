@@ -38,6 +38,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float round_bf16(float f) { return __uint_as_float(f32_to_bf16_bits(f) << 16); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
+__device__ __forceinline__ f32x4 as_f32x4(u32x4 w) { return __builtin_bit_cast(f32x4, w); }
 
 // acc + a.lo*b.lo + a.hi*b.hi for two packed bf16 pairs (v_dot2_f32_bf16; products exact in fp32).
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
@@ -101,6 +102,16 @@ __device__ __forceinline__ void store16_nt(void* p, u32x4 v) { __builtin_nontemp
 // A load whose range check fails returns zeros without a memory access.
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+// Device-scope forms (cache policy sc1): the store is written through to the level every XCD reads,
+// and the load is served from it, so data one block stores another block on any XCD can load once the
+// store has completed, without a fence that writes back or invalidates a whole L2.
+constexpr int kScDevice = 16;
+__device__ __forceinline__ void buffer_store16_dev(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kScDevice);
+}
+__device__ __forceinline__ u32x4 buffer_load16_dev(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kScDevice);
 }
 __device__ __forceinline__ f32x4 loadf4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 

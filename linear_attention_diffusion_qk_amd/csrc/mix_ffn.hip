@@ -199,6 +199,7 @@ hipError_t launch_mix_ffn(const uint16_t* x, const uint16_t* w1, const uint16_t*
                   rows_per_block);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  final_launch();
   return launch_gemm_bf16(gbuf, w2, out, M, F, C, stream, "gemm_project");
 }
 

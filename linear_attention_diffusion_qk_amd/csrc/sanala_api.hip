@@ -73,20 +73,23 @@ struct Timing {
 };
 thread_local Timing g_timing;
 
-// A call's hold on its stream's scratch.  While held, the kernels of the call carry the buffer's
-// last-use event as their stop event (launch_kernel); with kernel timing on they carry the timing
-// events instead, and the last-use event is recorded when the lease ends.
+// A call's hold on its stream's scratch.  While held, the call's last kernel carries the buffer's
+// last-use event as its stop event (launch_kernel after final_launch()); otherwise (kernel timing on,
+// or a path whose last launch did not carry it) the event is recorded when the lease ends.
 class ScratchLease {
  public:
   hipError_t acquire(int dev, hipStream_t stream, size_t bytes) {
     if (g_table.acquire(lease_, dev, stream, bytes) != 0) return hipErrorOutOfMemory;
-    if (!g_timing.enabled) {
-      sanala::stop_event() = static_cast<hipEvent_t>(lease_.event());
-      lease_.attached();
-    }
+    sanala::StopSignal& ss = sanala::stop_signal();
+    ss = sanala::StopSignal{};
+    if (!g_timing.enabled) ss.event = static_cast<hipEvent_t>(lease_.event());
     return hipSuccess;
   }
-  ~ScratchLease() { sanala::stop_event() = nullptr; }
+  ~ScratchLease() {
+    sanala::StopSignal& ss = sanala::stop_signal();
+    if (ss.event && ss.carried) lease_.attached();
+    ss = sanala::StopSignal{};
+  }
   void* ptr() const { return lease_.ptr(); }
 
  private:
@@ -157,9 +160,9 @@ hipError_t ensure_max_lds(const void* kernel, int bytes) {
   return e;
 }
 
-hipEvent_t& stop_event() {
-  thread_local hipEvent_t ev = nullptr;
-  return ev;
+StopSignal& stop_signal() {
+  thread_local StopSignal ss;
+  return ss;
 }
 
 bool timing_slot(const char* name, hipEvent_t* begin, hipEvent_t* end) {
