@@ -16,7 +16,7 @@ reduction and output: the whole path).
                                      # rocprofv3 --kernel-trace database -> per-kernel summary under profiles/
   python bench.py --summarize-counters WORKLOAD OUT.txt "COMMANDS" PMC.db...
                                      # rocprofv3 --pmc databases -> per-kernel counter summary (MFMA busy, waits, ...)
-  python bench.py --summarize-traffic KERNEL_FETCH.db KERNEL_WRITE.db COPY_FETCH.db COPY_WRITE.db
+  python bench.py --summarize-traffic KERNEL_FETCH.db KERNEL_WRITE.db COPY_FETCH.db COPY_WRITE.db [OUT [WORKLOAD [ENV]]]
                                      # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE databases -> profiles/hbm_traffic.txt
 """
 from __future__ import annotations
@@ -333,9 +333,12 @@ def _pmc_means(db: str, counter: str):
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
-def summarize_traffic(kfetch: str, kwrite: str, cfetch: str, cwrite: str, workload: str = "config4") -> str:
+def summarize_traffic(kfetch: str, kwrite: str, cfetch: str, cwrite: str, workload: str = "config4",
+                      env: str = "") -> str:
     """Per-dispatch HBM bytes of each libsanala kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
-    scaled by what the same counters read for a plain device copy of 268,435,456 bytes."""
+    scaled by what the same counters read for a plain device copy of 268,435,456 bytes.  `env`: the
+    environment settings the kernel runs were made with (shown in the commands)."""
+    pre = f"{env} " if env else ""
     copy_bytes = 256 * 1024 * 1024
     pick = lambda d: max((v for k, v in d.items() if "copy" in k.lower() or "elementwise" in k.lower()), default=None)  # noqa: E731
     cf, cw = pick(_pmc_means(cfetch, "FETCH_SIZE")), pick(_pmc_means(cwrite, "WRITE_SIZE"))
@@ -346,17 +349,17 @@ def summarize_traffic(kfetch: str, kwrite: str, cfetch: str, cwrite: str, worklo
              "# Counter KiB x 1024 x calibration; calibration = 268435456 / (counter bytes of a plain",
              "# device copy of 268435456 bytes, bench.py --mode copy).",
              "# Commands (from /tmp, TMPDIR=/tmp, one pass each):",
-             "#   rocprofv3 --pmc FETCH_SIZE -d kfetch -o run -- python3 /root/repo/bench.py --steps 2 --warmup 1 "
-             "--no-cpu-baseline --no-secondary --no-cold --workload config4",
-             "#   rocprofv3 --pmc WRITE_SIZE -d kwrite -o run -- (same bench command)",
+             f"#   {pre}rocprofv3 --pmc FETCH_SIZE -d kfetch -o run -- python3 /root/repo/bench.py --steps 2 --warmup 1 "
+             f"--no-cpu-baseline --no-secondary --no-cold --workload {workload}",
+             f"#   {pre}rocprofv3 --pmc WRITE_SIZE -d kwrite -o run -- (same bench command)",
              "#   rocprofv3 --pmc FETCH_SIZE -d cfetch -o run -- python3 /root/repo/bench.py --mode copy",
              "#   rocprofv3 --pmc WRITE_SIZE -d cwrite -o run -- python3 /root/repo/bench.py --mode copy",
              "#   python3 bench.py --summarize-traffic kfetch/run_results.db kwrite/run_results.db "
              "cfetch/run_results.db cwrite/run_results.db",
              f"workload: {workload}", f"source_hash: {source_hash()}",
              f"fetch_calibration: {f_scale:.4f}", f"write_calibration: {w_scale:.4f}"]
-    short = {"rowstats": "rowstats_k", "kv_state": "kv_state", "kv_reduce": "kv_reduce", "out_persist": "out",
-             "out_bf16": "out", "qkv_gemm": "qkv_gemm"}
+    short = {"rowstats": "rowstats_k", "kv_state_x": "kv_state_x", "kv_state": "kv_state", "kv_reduce": "kv_reduce",
+             "out_persist": "out", "out_bf16": "out", "qkv_gemm": "qkv_gemm"}
     for name in sorted(set(kf) | set(kw)):
         tag = next((v for k, v in short.items() if k in name), None)
         if tag is None or "sanala" not in name:
@@ -456,8 +459,11 @@ def main():
         print(text)
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-traffic":
-        text = summarize_traffic(*sys.argv[2:6])
-        with open(os.path.join(ROOT, "profiles", "hbm_traffic.txt"), "w") as f:
+        # --summarize-traffic KFETCH KWRITE CFETCH CWRITE [OUTFILE [WORKLOAD [ENV]]]
+        out = sys.argv[6] if len(sys.argv) > 6 else os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+        text = summarize_traffic(*sys.argv[2:6], workload=sys.argv[7] if len(sys.argv) > 7 else "config4",
+                                 env=sys.argv[8] if len(sys.argv) > 8 else "")
+        with open(out, "w") as f:
             f.write(text)
         print(text)
         return
