@@ -20,15 +20,32 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 
 # The current stream's raw handle without building a torch Stream object (that costs about 3 us a
-# call, which is a sixth of a 1024-token call); the public route is the fallback.
+# call, which is a sixth of a 1024-token call).  The accessor is private to torch, so it is used on a
+# device only after a first call has checked that it returns what the public route returns there; if
+# it is missing, raises, or disagrees, the public route is used from then on.
 _raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_raw_agrees: dict = {}  # device index -> whether the private accessor matched the public one
+
+
+def _raw_matches_public(dev: int) -> bool:
+    if _raw_current_stream is None:
+        return False
+    try:
+        return int(_raw_current_stream(dev)) == int(torch.cuda.current_stream(dev).cuda_stream)
+    except Exception:  # noqa: BLE001 - any failure means: do not use it
+        return False
 
 
 def _stream_handle(stream, like: Optional[torch.Tensor] = None) -> int:
     if stream is None:
-        if _raw_current_stream is not None and like is not None and like.device.index is not None:
-            return int(_raw_current_stream(like.device.index))
-        stream = torch.cuda.current_stream()
+        if like is not None and like.device.index is not None:
+            dev = like.device.index
+            ok = _raw_agrees.get(dev)
+            if ok is None:
+                ok = _raw_agrees[dev] = _raw_matches_public(dev)
+            if ok:
+                return int(_raw_current_stream(dev))
+        stream = torch.cuda.current_stream(like.device if like is not None and like.is_cuda else None)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 

@@ -86,3 +86,17 @@ def test_quantiser_pack_and_mix_ffn_checks():
         sanala.sana_mix_ffn_fwd(args[0], args[1], args[2][:F], args[3], 1, 2, 2, C, F, torch.zeros_like(xm))
     with pytest.raises(ValueError, match="out must hold"):
         sanala.sana_mix_ffn_fwd(*args, 1, 2, 2, C, F, torch.zeros(1, 3, C, dtype=torch.bfloat16))
+
+
+def test_private_stream_accessor_is_not_trusted_when_it_fails(monkeypatch):
+    """The binding uses torch's private current-stream accessor only after it agreed with the public
+    route; a missing or failing accessor means the public route."""
+    from linear_attention_diffusion_qk_amd import api
+
+    def broken(dev):
+        raise RuntimeError("no such accessor")
+
+    monkeypatch.setattr(api, "_raw_current_stream", broken)
+    assert api._raw_matches_public(0) is False
+    monkeypatch.setattr(api, "_raw_current_stream", None)
+    assert api._raw_matches_public(0) is False

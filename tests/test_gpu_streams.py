@@ -50,3 +50,13 @@ def test_many_streams_created_and_destroyed(gpu_lib):
     again = gpu_lib.linear_attn(q, k, v, gq, gk, inp.H)   # takes a new buffer
     torch.cuda.synchronize()
     assert torch.equal(again.view(torch.int16), ref.view(torch.int16))
+
+
+def test_binding_follows_torchs_current_stream(gpu_lib):
+    """Without an explicit stream the binding passes torch's current stream of the tensors' device."""
+    from linear_attention_diffusion_qk_amd import api
+    x = torch.empty(1, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert api._stream_handle(None, x) == s.cuda_stream
+    assert api._stream_handle(None, x) == torch.cuda.current_stream().cuda_stream
