@@ -7,6 +7,7 @@ the GPU side can take their inputs from it without sharing any computation.
 from .gen import (  # noqa: F401
     CONFIGS,
     AttnInputs,
+    CrossInputs,
     MixFfnInputs,
     QkvInputs,
     W8A8Inputs,
@@ -14,6 +15,7 @@ from .gen import (  # noqa: F401
     bf16_bits,
     gen_attn,
     gen_config,
+    gen_cross,
     gen_mix_ffn,
     gen_qkv,
     gen_w8a8,

@@ -15,7 +15,12 @@ GPU side can convert them without further rounding and the oracle can widen
 them to float64 exactly.
 
 Tensor ids: q=0, k=1, v=2, gq=3, gk=4, x=5, Wqkv=6, outlier rows=7, int8 weight codes=8,
-weight column scales=9, Mix-FFN W1=10, depthwise taps=11, W2=12.
+weight column scales=9, Mix-FFN W1=10, depthwise taps=11, W2=12, text-token keys=13, text-token
+values=14, text lengths=15.
+
+Cross-attention inputs stand in for the text encoder's projected embeddings (no encoder is run): the
+text-token keys and values are N(0,1) like the image-token queries, with up to 300 text tokens per
+sample (SANA's prompt length) and, for ragged batches, a seeded length per sample.
 """
 from __future__ import annotations
 
@@ -25,7 +30,7 @@ from typing import Optional
 import numpy as np
 
 (TID_Q, TID_K, TID_V, TID_GQ, TID_GK, TID_X, TID_W, TID_OUTLIER, TID_WCODE, TID_WSCALE, TID_W1, TID_KDW,
- TID_W2) = range(13)
+ TID_W2, TID_TK, TID_TV, TID_TLEN) = range(16)
 
 C_SANA = 2240
 H_SANA = 70
@@ -217,6 +222,51 @@ def gen_mix_ffn(cfg_id: int, B: int, Hg: int, Wg: int, C: int = C_SANA, F: int =
     kdw = _store(_rng(cfg_id, 0, TID_KDW).standard_normal((2 * F, 3, 3)) / 3.0, "bf16")
     w2 = _store(w_std * _rng(cfg_id, 0, TID_W2).standard_normal((F, C)), "bf16")
     return MixFfnInputs(np.stack(xs), w1, kdw, w2, Hg, Wg, name)
+
+
+@dataclass
+class CrossInputs:
+    q: np.ndarray            # [B, N, C] image-token queries
+    k: np.ndarray            # [B, L, C] text-token keys
+    v: np.ndarray            # [B, L, C] text-token values
+    gq: Optional[np.ndarray]
+    gk: Optional[np.ndarray]
+    kv_len: np.ndarray       # [B] int32, valid text tokens per sample (1..L)
+    H: int
+    D: int
+    eps: float
+    dtype: str
+    name: str = ""
+
+    @property
+    def B(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def N(self) -> int:
+        return self.q.shape[1]
+
+    @property
+    def L(self) -> int:
+        return self.k.shape[1]
+
+
+def gen_cross(cfg_id: int, B: int, N: int, L: int = 300, H: int = H_SANA, D: int = D_SANA, dtype: str = "bf16",
+              eps: float = EPS_SANA, norm: bool = True, ragged: bool = False, k_scale: float = 1.0,
+              name: str = "") -> CrossInputs:
+    """Queries ~ N(0,1) over N image tokens; text keys ~ k_scale*N(0,1) and values ~ N(0,1) over L text
+    tokens; with `ragged`, sample b has a seeded length in [1, L], else all L tokens are valid."""
+    C = H * D
+    qs, ks, vs, lens = [], [], [], []
+    for b in range(B):
+        qs.append(_store(_rng(cfg_id, b, TID_Q).standard_normal((N, C)), dtype))
+        ks.append(_store(k_scale * _rng(cfg_id, b, TID_TK).standard_normal((L, C)), dtype))
+        vs.append(_store(_rng(cfg_id, b, TID_TV).standard_normal((L, C)), dtype))
+        lens.append(int(_rng(cfg_id, b, TID_TLEN).integers(1, L + 1)) if ragged else L)
+    gq = gains(cfg_id, C, TID_GQ) if norm else None
+    gk = gains(cfg_id, C, TID_GK) if norm else None
+    return CrossInputs(np.stack(qs), np.stack(ks), np.stack(vs), gq, gk, np.asarray(lens, np.int32), H, D, eps,
+                       dtype, name)
 
 
 # The five SANA-shaped workloads (C = 2240 = 70 heads x 32).

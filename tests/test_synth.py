@@ -73,3 +73,15 @@ def test_qkv_config_shapes_small():
     assert inp.x.shape == (2, 8, 2240) and inp.w.shape == (2240, 6720)
     np.testing.assert_array_equal(bf16_round(inp.w), inp.w)
     assert abs(float(inp.w.std()) - 0.02) < 1e-3
+
+
+def test_cross_inputs_shapes_lengths_and_determinism():
+    from synth import gen_cross
+    a = gen_cross(21, 3, 40, L=50, H=4, ragged=True)
+    b = gen_cross(21, 3, 40, L=50, H=4, ragged=True)
+    assert a.q.shape == (3, 40, 128) and a.k.shape == (3, 50, 128) and a.v.shape == (3, 50, 128)
+    assert a.kv_len.dtype == np.int32 and ((a.kv_len >= 1) & (a.kv_len <= 50)).all()
+    assert all(np.array_equal(x, y) for x, y in ((a.q, b.q), (a.k, b.k), (a.v, b.v), (a.kv_len, b.kv_len)))
+    full = gen_cross(21, 2, 8, L=50, H=4)
+    assert (full.kv_len == 50).all() and full.gq is not None
+    assert gen_cross(21, 1, 8, L=5, H=4, norm=False).gq is None
