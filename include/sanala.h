@@ -186,6 +186,36 @@ sana_status_t sana_mix_ffn_fwd(const void* x, const void* W1, const void* Wdw, c
                                int B, int Hg, int Wg, int C, int F, void* out, hipStream_t stream);
 
 /*
+ * sana_cross_attn_fwd -- the Linear DiT block's cross-attention with QK-Norm ("SANA 1.5: Efficient
+ * Scaling of Training-Time and Inference-Time Compute in Linear Diffusion Transformer", research
+ * notes, model architecture: vanilla cross-attention injecting the text condition; QK Norm on its
+ * queries and keys).  Per sample b, head h (channels [32h, 32h+32)) and image token i:
+ *   qn = q * r_q * gq, kn = k * r_k * gk with r = 1/sqrt(mean over all C channels of x^2 + eps);
+ *   o[b,i,h] = sum_j softmax_j(qn[b,i,h] . kn[b,j,h] / sqrt(D)) v[b,j,h] over the text tokens
+ *   j < kv_len[b].  NULL gains: the norm is off.  The projections around it are the caller's.
+ *
+ *   q        device bf16 [B, N, C] image-token queries, C = H*D, contiguous, 16-byte aligned.
+ *   k, v     device bf16 [B, L, C] text-token keys and values, contiguous, 16-byte aligned.
+ *   gq, gk   device fp32 [C] RMSNorm gains, 16-byte aligned, or both NULL.
+ *   kv_len   device int32 [B]: valid text tokens of each sample (the rest is padding), or NULL for
+ *            all L.  Read on the device, so not checked: values are clamped to [0, L], and a sample with
+ *            0 valid tokens gets an all-zero output.
+ *   B >= 1 (<= 65535), N >= 1, 1 <= L <= 1024, D == 32, 1 <= H <= 128 (else SANA_ERR_UNSUPPORTED).
+ *   eps      finite, >= 0.
+ *   out      device bf16 [B, N, C], 16-byte aligned, not overlapping q, k or v; fully overwritten.
+ *   dtype    SANA_BF16 (others: SANA_ERR_UNSUPPORTED).
+ *
+ * Arithmetic: fp32 statistics; with the norm the keys enter the MFMA as bf16(k * r_k * gk) and the
+ * queries as bf16(q * r_q * gq) (without it, as given); logits as fp32 sums of the exact bf16 products,
+ * the 1/sqrt(D) scale and the softmax in fp32 (exp2), the softmax weights rounded to bf16 for the value
+ * product, fp32 accumulation, bf16 output (round to nearest even).
+ * Scratch (the stream's buffer): the normalised keys (B*L*C bf16) and r_q (B*N fp32).  Errors as above.
+ */
+sana_status_t sana_cross_attn_fwd(const void* q, const void* k, const void* v, const float* gq, const float* gk,
+                                  const int* kv_len, int B, int N, int L, int H, int D, float eps, void* out,
+                                  hipStream_t stream, sana_dtype_t dtype);
+
+/*
  * sana_quantize_rows_i8 -- per-row symmetric int8 quantisation of bf16 x [rows, C] (the activation
  * half of W8A8): with a = max_c |x[r, c]|, xq = clamp(rne(x * (127 / a)), -127, 127) and
  * x_scale[r] = a / 127, each step in fp32 with correctly rounded division; a row of zeros gives

@@ -23,7 +23,7 @@ SANA_F16 = 2
 
 # Every symbol include/sanala.h declares.
 EXPORTS = ("sana_linear_attn_fwd", "sana_linear_attn_fwd_noalloc", "sana_qkv_linear_attn_fwd", "sana_qkv_w8a8_linear_attn_fwd",
-           "sana_quantize_rows_i8", "sana_pack_weight_i8", "sana_mix_ffn_fwd", "sana_release_scratch",
+           "sana_quantize_rows_i8", "sana_pack_weight_i8", "sana_mix_ffn_fwd", "sana_cross_attn_fwd", "sana_release_scratch",
            "sana_status_string", "sana_timing_enable", "sana_timing_last")
 
 _lock = threading.Lock()
@@ -60,6 +60,8 @@ def load_library() -> ctypes.CDLL:
         lib.sana_pack_weight_i8.restype = ci
         lib.sana_mix_ffn_fwd.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, vp, vp]
         lib.sana_mix_ffn_fwd.restype = ci
+        lib.sana_cross_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, vp, vp, ci]
+        lib.sana_cross_attn_fwd.restype = ci
         lib.sana_release_scratch.argtypes = [vp]
         lib.sana_release_scratch.restype = ci
         lib.sana_status_string.argtypes = [ci]

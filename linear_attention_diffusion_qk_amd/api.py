@@ -190,6 +190,24 @@ def sana_mix_ffn_fwd(x, W1, Wdw, W2, B: int, Hg: int, Wg: int, C: int, F: int, o
         raise SanaError(st, "sana_mix_ffn_fwd")
 
 
+def sana_cross_attn_fwd(q, k, v, gq, gk, kv_len, B: int, N: int, L: int, H: int, D: int, eps: float, out,
+                        stream=None, dtype: Optional[int] = None) -> None:
+    """Same arguments as the C entry point; tensors stand in for the device pointers (kv_len: an int32
+    device tensor of B lengths, or None)."""
+    if dtype is None:
+        dtype = _lib.SANA_BF16
+    _need_sizes(B=B, N=N, L=L, H=H, D=D)
+    nq, nk, C = int(B) * int(N) * int(H) * int(D), int(B) * int(L) * int(H) * int(D), int(H) * int(D)
+    tdt = _NAMES_OF_DTYPE.get(int(dtype), torch.bfloat16)
+    _need([("q", q, nq, tdt), ("k", k, nk, tdt), ("v", v, nk, tdt), ("out", out, nq, tdt),
+           ("gq", gq, C, torch.float32), ("gk", gk, C, torch.float32), ("kv_len", kv_len, int(B), torch.int32)])
+    lib = _lib.load_library()
+    st = lib.sana_cross_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gq), _ptr(gk), _ptr(kv_len), int(B), int(N), int(L),
+                                 int(H), int(D), float(eps), _ptr(out), _stream_handle(stream, q), int(dtype))
+    if st != _lib.SANA_OK:
+        raise SanaError(st, "sana_cross_attn_fwd")
+
+
 def sana_release_scratch(stream=None) -> None:
     """Frees the library's scratch buffer of `stream` (default: the current stream) on the current device,
     stream-ordered; call it before destroying a stream the library has used."""
@@ -216,6 +234,26 @@ def linear_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gq: Optional[
         out = torch.empty_like(q)
     _same_as("out", out, q)
     sana_linear_attn_fwd(q, k, v, gq, gk, B, N, H, D, eps, out)
+    return out
+
+
+def cross_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gq: Optional[torch.Tensor],
+               gk: Optional[torch.Tensor], H: int, D: int = 32, eps: float = 1e-6,
+               kv_len: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Softmax cross-attention with QK-Norm: q [B, N, H*D] image tokens, k, v [B, L, H*D] text tokens,
+    all bfloat16; kv_len: int32 [B] valid text tokens per sample (None: all L)."""
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2]:
+        raise ValueError("q must be [B, N, C] and k, v [B, L, C] with the same B and C")
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must be bfloat16")
+    B, N, C = q.shape
+    L = k.shape[1]
+    if C != H * D:
+        raise ValueError(f"last dim {C} != H*D = {H}*{D}")
+    if out is None:
+        out = torch.empty_like(q)
+    _same_as("out", out, q)
+    sana_cross_attn_fwd(q, k, v, gq, gk, kv_len, B, N, L, H, D, eps, out)
     return out
 
 

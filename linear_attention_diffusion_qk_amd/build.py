@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsanala.so")
-SOURCES = ["attn_plan.hip", "attn_f32.hip", "attn_bf16.hip", "kv_state_x.hip", "gemm_kernel.hip", "mix_ffn.hip", "sanala_api.hip"]
+SOURCES = ["attn_plan.hip", "attn_f32.hip", "attn_bf16.hip", "kv_state_x.hip", "gemm_kernel.hip", "mix_ffn.hip", "cross_attn.hip", "sanala_api.hip"]
 ARCH = os.environ.get("SANA_OFFLOAD_ARCH", "gfx950")
 
 # Packed-FP32 VALU instructions are kept out of the device code on purpose.

@@ -98,6 +98,16 @@ hipError_t launch_mix_ffn(const uint16_t* x, const uint16_t* w1, const uint16_t*
                           int Wg, int C, int F, uint16_t* out, void* ws, hipStream_t stream);
 size_t mix_ffn_workspace_bytes(int64_t M, int C, int F);
 int mix_ffn_max_width();
+// Cross-attention with QK-Norm (cross_attn.hip): q, out [B, N, 32H]; k, v [B, L, 32H]; all bf16; gq, gk
+// [32H] or both NULL; kv_len [B] int32 on the device or NULL.  ws holds
+// cross_attn_workspace_bytes(B, N, L, H) bytes.  L <= cross_attn_max_keys(), H <= cross_attn_max_heads().
+hipError_t launch_cross_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gq, const float* gk,
+                             const int* kv_len, int B, int N, int L, int H, float eps, uint16_t* out, void* ws,
+                             hipStream_t stream);
+size_t cross_attn_workspace_bytes(int64_t B, int64_t N, int64_t L, int H);
+int cross_attn_max_keys();
+int cross_attn_max_heads();
+
 // int8 [rows, C] row-major -> K-blocked [C/64][rows][64] (C a multiple of 64).
 hipError_t launch_pack_k64(const int8_t* src, int64_t rows, int C, int8_t* dst, hipStream_t stream);
 

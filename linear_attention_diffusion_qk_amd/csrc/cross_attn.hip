@@ -1,0 +1,268 @@
+// Cross-attention with QK-Norm on gfx950: queries from the image tokens, keys and values from the text
+// tokens, softmax over each sample's valid text tokens ("SANA 1.5: Efficient Scaling of Training-Time
+// and Inference-Time Compute in Linear Diffusion Transformer" (research notes), model architecture: the
+// Linear DiT block's vanilla cross-attention, and the QK Norm bullet: RMSNorm on its queries and keys).
+//
+// Launches on one stream:
+//   cross_prep  (QK-Norm on) one wave per row.  Text tokens: r_k = 1/sqrt(mean_c k^2 + eps) and
+//               k^ = bf16(k * r_k * gk), the normalised keys the MFMA takes.  Image tokens: r_q.
+//               Norm off: no launch, k^ = k.
+//   cross_attn  block = (chunk of queries, head, sample), 4 waves.  The head's k^ and v of the sample go
+//               to LDS once per block (k^ row-major with an XOR swizzle, v transposed); then each wave
+//               takes 32 queries at a time: q^ = bf16(q * r_q * gq) in registers, S^T = k^ q^T on
+//               v_mfma_f32_32x32x16_bf16, so that a lane holds one query's logits for 16 of every 32
+//               keys and the softmax's max and sum are in-lane plus one exchange between the two lane
+//               halves.  The logits stay exact products of the bf16 operands (fp32 sums); the softmax
+//               scale log2(e)/sqrt(D) is applied in fp32 inside the exponent's multiply-add, since
+//               folding it into bf16 keys would round logits of a few hundred (no norm) by a whole unit.
+//               Keys go in chunks of 128 with the running max and sum rescaled between chunks;
+//               P = exp2(sc (s - max)) is rounded to bf16 and O^T = V^T P^T runs on the same MFMA with P taken
+//               straight from the S^T registers: the MFMA's k index runs over the keys in the order the
+//               accumulator holds them (lane half g: keys 4g..4g+3 and 8+4g..8+4g+3 of each 16), and V^T
+//               is read from LDS in that order.  o = O / sum, stored as bf16.
+#include "common.h"
+
+#include <algorithm>
+#include <cmath>
+
+namespace sanala {
+
+namespace {
+constexpr int kCrossChunk = 128;  // keys per softmax chunk: 4 MFMA tiles of 32
+constexpr int kCrossPrepUnits = 8;  // 16-byte units per lane in cross_prep: rows of up to 4096 channels
+constexpr float kLog2e = 1.4426950408889634f;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Byte offset of 16-byte unit u (dims 8u..8u+7) of key j in the staged k^ tile (64-byte rows).  The
+// XOR with bits 2-3 of j puts the same unit of any 16 consecutive keys in 16 different bank slots.
+__device__ __forceinline__ int khat_off(int j, int u) { return j * 64 + 16 * (u ^ ((j >> 2) & 3)); }
+}  // namespace
+
+// Rows [0, krows): text tokens of k -> khat; rows [krows, krows + qrows): r_q of q.
+__global__ __launch_bounds__(256) void cross_prep(const uint16_t* __restrict__ k, const uint16_t* __restrict__ q,
+                                                  const float* __restrict__ gk, int64_t krows, int64_t qrows, int C,
+                                                  float eps, uint16_t* __restrict__ khat, float* __restrict__ r_q) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= krows + qrows) return;
+  const bool is_k = row < krows;  // uniform per wave
+  const uint16_t* src = is_k ? k + row * C : q + (row - krows) * C;
+  const int nvec = C / 8;
+  u32x4 w[kCrossPrepUnits];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < kCrossPrepUnits; ++j) {
+    const int i = lane + 64 * j;
+    w[j] = i < nvec ? load16(src + 8 * i) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ss = dot2_bf16(w[j][u], w[j][u], ss);
+  }
+  const float r = 1.0f / sqrtf(wave_sum(ss) / (float)C + eps);
+  if (!is_k) {
+    if (lane == 0) r_q[row - krows] = r;
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < kCrossPrepUnits; ++j) {
+    const int i = lane + 64 * j;
+    if (i < nvec) {
+      const f32x4 g0 = loadf4(gk + 8 * i), g1 = loadf4(gk + 8 * i + 4);
+      const float g[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+      u32x4 o;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        o[u] = cvt_pk_bf16(bf16_lo(w[j][u]) * r * g[2 * u], bf16_hi(w[j][u]) * r * g[2 * u + 1]);
+      store16(khat + row * C + 8 * i, o);
+    }
+  }
+}
+
+// q, out: [B, N, C]; khat (k itself without the norm), v: [B, L, C]; C = 32 H; sc = log2(e)/sqrt(D).
+// kv_len: valid text tokens per sample (NULL: L), clamped to [0, L]; a sample with none gets zeros.
+// Block (x, h, b): query tiles x*4*qtiles .. x*4*qtiles + 4*qtiles - 1 of 32 queries, wave w taking
+// every fourth.
+template <bool NORM>
+__global__ __launch_bounds__(256) void cross_attn_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ khat,
+                                                       const uint16_t* __restrict__ v, const float* __restrict__ r_q,
+                                                       const float* __restrict__ gq, const int* __restrict__ kv_len,
+                                                       int N, int L, int Lp, int H, int qtiles, float sc,
+                                                       uint16_t* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  char* const Ks = lds;                          // Lp keys x 64 bytes, swizzled (khat_off)
+  uint16_t* const Vt = reinterpret_cast<uint16_t*>(lds + Lp * 64);  // 32 dims x vpitch bf16 (v transposed)
+  const int vpitch = Lp + 4;  // in bf16: 2*Lp + 8 bytes, an odd multiple of 8 bytes, so the 32 rows of
+                              // an 8-byte read at one key offset fall in 32 different bank pairs
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int C = H * kHeadDim;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int ql = lane & 31, hf = lane >> 5;
+  const int kvl = kv_len ? min(max(kv_len[b], 0), L) : L;
+
+  // Stage k^ and v^T of head h (keys past L are zero).
+  const int64_t kv0 = (int64_t)b * L;
+  for (int i = tid; i < Lp * 4; i += 256) {
+    const int j = i >> 2, u = i & 3;
+    u32x4 kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+    if (j < L) {
+      kk = load16(khat + (kv0 + j) * C + h * kHeadDim + 8 * u);
+      vv = load16(v + (kv0 + j) * C + h * kHeadDim + 8 * u);
+    }
+    store16(Ks + khat_off(j, u), kk);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      Vt[(8 * u + e) * vpitch + j] = (uint16_t)((e & 1) ? (vv[e >> 1] >> 16) : (vv[e >> 1] & 0xffffu));
+  }
+
+  // Query gains of this lane's dims: 8hf..8hf+7 (first 16-dim step) and 16+8hf..16+8hf+7 (second).
+  float g[2][8];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) g[ks][e] = NORM ? gq[h * kHeadDim + 16 * ks + 8 * hf + e] : 1.f;
+  __syncthreads();
+
+  const int nchunks = (kvl + kCrossChunk - 1) / kCrossChunk;
+  const int64_t qrow0 = (int64_t)b * N;
+  const int tile0 = blockIdx.x * 4 * qtiles;
+  auto qload = [&](int t, u32x4& qa, u32x4& qb, float& rq) {
+    const int n = min((tile0 + 4 * t + w) * 32 + ql, N - 1);
+    const uint16_t* qr = q + (qrow0 + n) * C + h * kHeadDim + 8 * hf;
+    qa = load16(qr);
+    qb = load16(qr + 16);
+    rq = NORM ? r_q[qrow0 + n] : 1.f;
+  };
+  u32x4 qa, qb;
+  float rq;
+  qload(0, qa, qb, rq);
+  for (int t = 0; t < qtiles; ++t) {
+    const int n0 = (tile0 + 4 * t + w) * 32;
+    if (n0 >= N) break;  // uniform per wave; later tiles of this wave start further on
+    // q^ = bf16(q * r_q * gq); the next tile's loads go out now.
+    u32x4 qh[2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      qh[0][u] = NORM ? cvt_pk_bf16(bf16_lo(qa[u]) * rq * g[0][2 * u], bf16_hi(qa[u]) * rq * g[0][2 * u + 1]) : qa[u];
+      qh[1][u] = NORM ? cvt_pk_bf16(bf16_lo(qb[u]) * rq * g[1][2 * u], bf16_hi(qb[u]) * rq * g[1][2 * u + 1]) : qb[u];
+    }
+    if (t + 1 < qtiles) qload(t + 1, qa, qb, rq);
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 o;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[r] = 0.f;
+    for (int ch = 0; ch < nchunks; ++ch) {
+      const int j0 = ch * kCrossChunk;
+      const int ntiles = min(kCrossChunk / 32, (kvl - j0 + 31) / 32);  // tiles holding a valid key
+      f32x16 s[kCrossChunk / 32];
+#pragma unroll
+      for (int tt = 0; tt < kCrossChunk / 32; ++tt) {
+        if (tt < ntiles) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[tt][r] = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const u32x4 a = load16(Ks + khat_off(j0 + 32 * tt + ql, 2 * ks + hf));
+            s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qh[ks]), s[tt], 0, 0, 0);
+          }
+        }
+      }
+      // s[tt][r]: query n0 + ql, key j0 + 32 tt + 8 (r / 4) + 4 hf + r % 4 (logit before the scale sc).
+      float mc = -INFINITY;
+#pragma unroll
+      for (int tt = 0; tt < kCrossChunk / 32; ++tt) {
+        if (tt < ntiles) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j0 + 32 * tt + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (key >= kvl) s[tt][r] = -INFINITY;
+            mc = fmaxf(mc, s[tt][r]);
+          }
+        }
+      }
+      mc = fmaxf(mc, __shfl_xor(mc, 32));
+      const float m_new = fmaxf(m_run, mc);  // finite: the chunk holds a valid key
+      const float alpha = __builtin_amdgcn_exp2f(sc * (m_run - m_new));  // 0 for the first chunk
+      const float cm = -sc * m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[r] *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int tt = 0; tt < kCrossChunk / 32; ++tt) {
+        if (tt < ntiles) {
+          uint32_t pk[8];
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[tt][r], sc, cm));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[tt][r + 1], sc, cm));
+            l_run += p0 + p1;
+            pk[r >> 1] = cvt_pk_bf16(p0, p1);
+          }
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int kb = j0 + 32 * tt + 16 * jj + 4 * hf;
+            const u32x2 a0 = *reinterpret_cast<const u32x2*>(Vt + ql * vpitch + kb);
+            const u32x2 a1 = *reinterpret_cast<const u32x2*>(Vt + ql * vpitch + kb + 8);
+            const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
+            const u32x4 bp = {pk[4 * jj], pk[4 * jj + 1], pk[4 * jj + 2], pk[4 * jj + 3]};
+            o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bp), o, 0, 0, 0);
+          }
+        }
+      }
+    }
+    // o[r]: dim 8 (r / 4) + 4 hf + r % 4 of query n0 + ql.
+    const float lt = l_run + __shfl_xor(l_run, 32);
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const int n = n0 + ql;
+    if (n < N) {
+      uint16_t* orow = out + (qrow0 + n) * C + h * kHeadDim + 4 * hf;
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const u32x2 pv = {cvt_pk_bf16(o[4 * gi] * inv, o[4 * gi + 1] * inv),
+                          cvt_pk_bf16(o[4 * gi + 2] * inv, o[4 * gi + 3] * inv)};
+        __builtin_nontemporal_store(pv, reinterpret_cast<u32x2*>(orow + 8 * gi));
+      }
+    }
+  }
+}
+
+size_t cross_attn_workspace_bytes(int64_t B, int64_t N, int64_t L, int H) {
+  const size_t khat = ((size_t)B * L * H * kHeadDim * 2 + 255) / 256 * 256;
+  return khat + (size_t)B * N * 4;
+}
+
+int cross_attn_max_keys() { return 1024; }
+int cross_attn_max_heads() { return 64 * kCrossPrepUnits * 8 / kHeadDim; }
+
+hipError_t launch_cross_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gq, const float* gk,
+                             const int* kv_len, int B, int N, int L, int H, float eps, uint16_t* out, void* ws,
+                             hipStream_t stream) {
+  const int C = H * kHeadDim;
+  uint16_t* khat = static_cast<uint16_t*>(ws);
+  float* r_q = reinterpret_cast<float*>(static_cast<char*>(ws) + ((size_t)B * L * C * 2 + 255) / 256 * 256);
+  const bool norm = gq != nullptr;
+  const int64_t krows = (int64_t)B * L, qrows = (int64_t)B * N;
+  const float c = kLog2e / std::sqrt((float)kHeadDim);
+  if (norm)
+    launch_kernel("cross_prep", cross_prep, (unsigned)((krows + qrows + 3) / 4), 256, 0, stream, k, q, gk, krows, qrows,
+                  C, eps, khat, r_q);
+  const uint16_t* kh = norm ? khat : k;
+  const int Lp = (L + 31) / 32 * 32;
+  const size_t lds = (size_t)Lp * 64 + (size_t)kHeadDim * (Lp + 4) * 2;
+  const int qtiles = N >= 8192 ? 4 : N >= 2048 ? 2 : 1;  // 32-query tiles per wave
+  const dim3 grid((unsigned)((N + 128 * qtiles - 1) / (128 * qtiles)), (unsigned)H, (unsigned)B);
+  const void* kern = norm ? reinterpret_cast<const void*>(&cross_attn_bf16<true>)
+                          : reinterpret_cast<const void*>(&cross_attn_bf16<false>);
+  const hipError_t ea = ensure_max_lds(kern, 160 * 1024);
+  if (ea != hipSuccess) return ea;
+  final_launch();
+  if (norm)
+    launch_kernel("cross_attn", cross_attn_bf16<true>, grid, 256, lds, stream, q, kh, v, r_q, gq, kv_len, N, L, Lp, H,
+                  qtiles, c, out);
+  else
+    launch_kernel("cross_attn", cross_attn_bf16<false>, grid, 256, lds, stream, q, kh, v, r_q, gq, kv_len, N, L, Lp, H,
+                  qtiles, c, out);
+  return hipGetLastError();
+}
+
+}  // namespace sanala

@@ -352,6 +352,36 @@ extern "C" sana_status_t sana_mix_ffn_fwd(const void* x, const void* W1, const v
   return e == hipSuccess ? SANA_OK : SANA_ERR_HIP;
 }
 
+extern "C" sana_status_t sana_cross_attn_fwd(const void* q, const void* k, const void* v, const float* gq,
+                                             const float* gk, const int* kv_len, int B, int N, int L, int H, int D,
+                                             float eps, void* out, hipStream_t stream, sana_dtype_t dtype) {
+  if (!q || !k || !v || !out) return SANA_ERR_INVALID_ARG;
+  if (dtype != SANA_F32 && dtype != SANA_BF16 && dtype != SANA_F16) return SANA_ERR_INVALID_ARG;
+  if (B <= 0 || N <= 0 || L <= 0 || H <= 0 || D <= 0) return SANA_ERR_INVALID_ARG;
+  if (!std::isfinite(eps) || eps < 0.f || (gq == nullptr) != (gk == nullptr)) return SANA_ERR_INVALID_ARG;
+  if (dtype != SANA_BF16 || D != sanala::kHeadDim || H > sanala::cross_attn_max_heads() ||
+      L > sanala::cross_attn_max_keys() || B > 65535)
+    return SANA_ERR_UNSUPPORTED;
+  const double qelems = (double)B * N * H * D;
+  if (qelems >= 1099511627776.0) return SANA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (gq && !aligned16(gq)) ||
+      (gk && !aligned16(gk)) || (reinterpret_cast<uintptr_t>(kv_len) & 3))
+    return SANA_ERR_MISALIGNED;
+  const size_t qbytes = (size_t)B * N * H * D * 2, kbytes = (size_t)B * L * H * D * 2;
+  if (overlaps(out, qbytes, q, qbytes) || overlaps(out, qbytes, k, kbytes) || overlaps(out, qbytes, v, kbytes))
+    return SANA_ERR_INVALID_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SANA_ERR_HIP;
+  init_pool(dev);
+  g_timing.count = 0;
+  ScratchLease lease;
+  if (lease.acquire(dev, stream, sanala::cross_attn_workspace_bytes(B, N, L, H)) != hipSuccess) return SANA_ERR_HIP;
+  const hipError_t e = sanala::launch_cross_attn(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                                 static_cast<const uint16_t*>(v), gq, gk, kv_len, B, N, L, H, eps,
+                                                 static_cast<uint16_t*>(out), lease.ptr(), stream);
+  return e == hipSuccess ? SANA_OK : SANA_ERR_HIP;
+}
+
 extern "C" sana_status_t sana_quantize_rows_i8(const void* x, int64_t rows, int C, void* xq, float* x_scale,
                                                hipStream_t stream) {
   if (!x || !xq || !x_scale || rows < 1 || C < 1) return SANA_ERR_INVALID_ARG;
