@@ -47,7 +47,14 @@ WORKLOADS = {
                              "with column scales -> linear attention H=70, D=32 on bf16 qkv"),
     "mixffn": dict(cfg=5, desc="2K Mix-FFN: x[4, 64x64, 2240] bf16 @ W1[2240,11200] -> 3x3 depthwise conv (zero pad) "
                                "-> GLU -> @ W2[5600,2240]"),
+    "cross4k": dict(cfg=6, N=16384, desc="4K cross-attention with QK-RMSNorm: B=1, N=16384 image tokens (128x128 "
+                                         "latent), L=300 text tokens, H=70, D=32, bf16"),
+    "cross1k": dict(cfg=6, N=1024, desc="1024px cross-attention with QK-RMSNorm: B=1, N=1024 image tokens, L=300 text "
+                                        "tokens, H=70, D=32, bf16"),
 }
+# Cross-attention: the softmax's exp2 runs on the vector ALU at a quarter of the fp32 rate; from the
+# fp32 vector peak (157.3 TFLOP/s = 78.6 T fused multiply-adds/s) that is 19.66 T exponentials/s.
+EXP2_PEAK_T = 157.3 / 2 / 4
 
 
 def log(*a):
@@ -95,16 +102,23 @@ class Inputs:
             from synth import gen_mix_ffn
             inp = gen_mix_ffn(self.spec["cfg"], 4, 64, 64)
             self.kind = "mixffn"
+        elif name.startswith("cross"):
+            from synth import gen_cross
+            inp = gen_cross(self.spec["cfg"], 1, self.spec["N"], L=300)
+            self.kind = "cross"
         else:
             inp = gen_config(self.spec["cfg"])
             self.kind = "qkv" if self.spec["cfg"] == 5 else "attn"
         self.host = inp
         bf = torch.bfloat16
         g = lambda a: torch.from_numpy(a).to("cuda")  # noqa: E731
-        if self.kind == "attn":
+        if self.kind in ("attn", "cross"):
             tdt = torch.float32 if inp.dtype == "f32" else bf
             self.q, self.k, self.v = (torch.from_numpy(a).to("cuda").to(tdt) for a in (inp.q, inp.k, inp.v))
             self.out = torch.empty_like(self.q)
+            if self.kind == "cross":
+                self.kv_len = torch.from_numpy(inp.kv_len).to("cuda")
+                self.L = inp.L
         elif self.kind == "qkv":
             self.x = torch.from_numpy(inp.x).to("cuda").to(bf)
             self.w = torch.from_numpy(inp.w).to("cuda").to(bf)
@@ -140,6 +154,9 @@ class Inputs:
         elif self.kind == "mixffn":
             sanala.sana_mix_ffn_fwd(self.x, self.w1, self.kdw, self.w2, self.B, self.host.Hg, self.host.Wg, self.C,
                                     self.host.F, self.out)
+        elif self.kind == "cross":
+            sanala.sana_cross_attn_fwd(self.q, self.k, self.v, self.gq, self.gk, self.kv_len, self.B, self.N, self.L,
+                                       self.H, self.D, self.host.eps, self.out)
         else:
             sanala.sana_qkv_w8a8_linear_attn_fwd(self.x, self.wt, self.sw, self.gq, self.gk, self.B, self.N, self.H,
                                                  self.D, self.host.eps, self.out)
@@ -149,7 +166,10 @@ class Inputs:
         return 4 if getattr(self.host, "dtype", "bf16") == "f32" else 2
 
     def algorithmic_bytes(self) -> int:
-        """Read Q, K, V and write O once: 4 * B * N * C * element size bytes."""
+        """Read Q, K, V and write O once: 4 * B * N * C * element size bytes (cross-attention: Q and O over
+        the N image tokens, K and V over the L text tokens)."""
+        if self.kind == "cross":
+            return 2 * self.B * (self.N + self.L) * self.C * self.esize
         return 4 * self.B * self.N * self.C * self.esize
 
     def kernel_bytes(self, kernel: str) -> float:
@@ -162,6 +182,8 @@ class Inputs:
             return tok                # read one tensor
         if kernel == "fused":
             return 4 * tok
+        if kernel == "cross_attn":
+            return self.algorithmic_bytes()
         return 0.0
 
 
@@ -296,6 +318,8 @@ def cpu_baseline(inputs: Inputs, min_seconds: float = 12.0, max_reps: int = 200)
             oracle.qkv_linear_attn(h.x, h.w, h.gq, h.gk, h.H, h.D, h.eps)
         elif inputs.kind == "mixffn":
             oracle.mix_ffn(h.x, h.w1, h.kdw, h.w2, h.Hg, h.Wg)
+        elif inputs.kind == "cross":
+            oracle.cross_attn(h.q, h.k, h.v, h.gq, h.gk, h.H, h.D, h.eps, kv_len=h.kv_len)
         else:
             oracle.qkv_w8a8_linear_attn(h.x, h.wt_q, h.s_w, h.gq, h.gk, h.H, h.D, h.eps)
         reps += 1
@@ -503,7 +527,7 @@ def main():
     log(f"[bench] {args.workload}: {ms * 1e3:.1f} us/step, {value:.4g} tokens/s, {call_gbps:.0f} GB/s algorithmic")
     cold = None
     flush = None
-    if not args.no_cold and main_in.kind in ("attn", "qkv", "w8a8"):
+    if not args.no_cold and main_in.kind in ("attn", "qkv", "w8a8", "cross"):
         flush = CacheFlush()
         cms = time_cold(main_in, sanala, args.steps, max(1, args.warmup // 2), flush)
         cold = point(main_in, cms)
@@ -525,6 +549,21 @@ def main():
         roof["dwconv_glu"] = {"bound": "hbm", "achieved": round(cb / (conv_ms * 1e-3) / 1e9, 1),
                               "peak": HBM_PEAK_GBPS, "unit": "GB/s", "algorithmic_per_launch": cb,
                               "avg_launch_us": round(conv_ms * 1e3, 2)}
+    elif main_in.kind == "cross":
+        # The dominant kernel is bound by the softmax's exponentials on the vector ALU: one per (image token,
+        # valid text token, head); its HBM rate and MFMA rate are given beside it.
+        cms = kt.get("cross_attn", float("nan"))
+        exps = float(main_in.N * int(main_in.kv_len.sum().item()) * main_in.H)
+        ach = exps / (cms * 1e-3) / 1e12
+        flops = 4.0 * main_in.N * int(main_in.kv_len.sum().item()) * main_in.C
+        kb = main_in.algorithmic_bytes()
+        roof = {"bound": "alu", "kernel": "cross_attn", "achieved": round(ach, 2), "peak": round(EXP2_PEAK_T, 2),
+                "unit": "T exp2/s", "frac": round(ach / EXP2_PEAK_T, 4), "traffic": None,
+                "avg_launch_us": round(cms * 1e3, 2), "algorithmic_per_launch": exps,
+                "hbm": {"achieved": round(kb / (cms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "algorithmic_per_launch": kb},
+                "mfma": {"achieved": round(flops / (cms * 1e-3) / 1e12, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "algorithmic_per_launch": flops}}
     elif main_in.kind in ("qkv", "w8a8"):
         gname = "qkv_gemm" if main_in.kind == "qkv" else "qkv_gemm_i8"
         peak = MFMA_BF16_PEAK_TFLOPS if main_in.kind == "qkv" else MFMA_I8_PEAK_TOPS

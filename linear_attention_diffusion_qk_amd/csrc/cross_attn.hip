@@ -7,7 +7,7 @@
 //   cross_prep  (QK-Norm on) one wave per row.  Text tokens: r_k = 1/sqrt(mean_c k^2 + eps) and
 //               k^ = bf16(k * r_k * gk), the normalised keys the MFMA takes.  Image tokens: r_q.
 //               Norm off: no launch, k^ = k.
-//   cross_attn  block = (chunk of queries, head, sample), 4 waves.  The head's k^ and v of the sample go
+//   cross_attn  block = (chunk of queries, head, sample), 8 waves.  The head's k^ and v of the sample go
 //               to LDS once per block (k^ row-major with an XOR swizzle, v transposed); then each wave
 //               takes 32 queries at a time: q^ = bf16(q * r_q * gq) in registers, S^T = k^ q^T on
 //               v_mfma_f32_32x32x16_bf16, so that a lane holds one query's logits for 16 of every 32
@@ -15,20 +15,24 @@
 //               halves.  The logits stay exact products of the bf16 operands (fp32 sums); the softmax
 //               scale log2(e)/sqrt(D) is applied in fp32 inside the exponent's multiply-add, since
 //               folding it into bf16 keys would round logits of a few hundred (no norm) by a whole unit.
-//               Keys go in chunks of 128 with the running max and sum rescaled between chunks;
-//               P = exp2(sc (s - max)) is rounded to bf16 and O^T = V^T P^T runs on the same MFMA with P taken
+//               The softmax here costs more vector-ALU work per logit (a quarter-rate exp2 among about
+//               six operations) than the MFMA work, so the logits are formed twice rather than kept:
+//               one pass for the row maximum, one for P = exp2(sc (s - max)), its sum and the value
+//               product.  P is rounded to bf16 (its row sum taken over those rounded values) and
+//               O^T = V^T P^T runs on the same MFMA with P taken
 //               straight from the S^T registers: the MFMA's k index runs over the keys in the order the
 //               accumulator holds them (lane half g: keys 4g..4g+3 and 8+4g..8+4g+3 of each 16), and V^T
 //               is read from LDS in that order.  o = O / sum, stored as bf16.
 #include "common.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 
 namespace sanala {
 
 namespace {
-constexpr int kCrossChunk = 128;  // keys per softmax chunk: 4 MFMA tiles of 32
+constexpr int kCrossWaves = 8;      // waves per cross_attn block: they share one staged head
 constexpr int kCrossPrepUnits = 8;  // 16-byte units per lane in cross_prep: rows of up to 4096 channels
 constexpr float kLog2e = 1.4426950408889634f;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -79,13 +83,14 @@ __global__ __launch_bounds__(256) void cross_prep(const uint16_t* __restrict__ k
 
 // q, out: [B, N, C]; khat (k itself without the norm), v: [B, L, C]; C = 32 H; sc = log2(e)/sqrt(D).
 // kv_len: valid text tokens per sample (NULL: L), clamped to [0, L]; a sample with none gets zeros.
-// Block (x, h, b): query tiles x*4*qtiles .. x*4*qtiles + 4*qtiles - 1 of 32 queries, wave w taking
-// every fourth.
+// Block (x, h, b) of W = kCrossWaves waves, gridDim.x = P blocks per (head, sample), sized so that the
+// whole grid is resident at once: the block stages head h once and takes the 32-query tiles
+// x, x + P, x + 2P, ..., wave w every W-th of those.
 template <bool NORM>
-__global__ __launch_bounds__(256) void cross_attn_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ khat,
+__global__ __launch_bounds__(64 * kCrossWaves, 4) void cross_attn_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ khat,
                                                        const uint16_t* __restrict__ v, const float* __restrict__ r_q,
                                                        const float* __restrict__ gq, const int* __restrict__ kv_len,
-                                                       int N, int L, int Lp, int H, int qtiles, float sc,
+                                                       int N, int L, int Lp, int H, float sc,
                                                        uint16_t* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   char* const Ks = lds;                          // Lp keys x 64 bytes, swizzled (khat_off)
@@ -98,34 +103,44 @@ __global__ __launch_bounds__(256) void cross_attn_bf16(const uint16_t* __restric
   const int ql = lane & 31, hf = lane >> 5;
   const int kvl = kv_len ? min(max(kv_len[b], 0), L) : L;
 
-  // Stage k^ and v^T of head h (keys past L are zero).
+  // Stage k^ and v^T of head h (keys past L are zero), and the largest squared norm of a valid key
+  // (the four lanes holding one key's four units are adjacent).
+  __shared__ float kmax_w[kCrossWaves];
   const int64_t kv0 = (int64_t)b * L;
-  for (int i = tid; i < Lp * 4; i += 256) {
+  float kmax = 0.f;
+  for (int i = tid; i < Lp * 4; i += 64 * kCrossWaves) {
     const int j = i >> 2, u = i & 3;
     u32x4 kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
     if (j < L) {
       kk = load16(khat + (kv0 + j) * C + h * kHeadDim + 8 * u);
       vv = load16(v + (kv0 + j) * C + h * kHeadDim + 8 * u);
     }
+    float kn = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kn = dot2_bf16(kk[e], kk[e], kn);
+    kn += __shfl_xor(kn, 1);
+    kn += __shfl_xor(kn, 2);
+    if (j < kvl) kmax = fmaxf(kmax, kn);
     store16(Ks + khat_off(j, u), kk);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       Vt[(8 * u + e) * vpitch + j] = (uint16_t)((e & 1) ? (vv[e >> 1] >> 16) : (vv[e >> 1] & 0xffffu));
   }
+#pragma unroll
+  for (int o = 32; o >= 4; o >>= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, o));
+  if (lane == 0) kmax_w[w] = kmax;
 
-  // Query gains of this lane's dims: 8hf..8hf+7 (first 16-dim step) and 16+8hf..16+8hf+7 (second).
-  float g[2][8];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) g[ks][e] = NORM ? gq[h * kHeadDim + 16 * ks + 8 * hf + e] : 1.f;
   __syncthreads();
 
-  const int nchunks = (kvl + kCrossChunk - 1) / kCrossChunk;
+  const int ktiles = (kvl + 31) / 32;  // key tiles holding a valid key
+  kmax = kmax_w[0];
+#pragma unroll
+  for (int i = 1; i < kCrossWaves; ++i) kmax = fmaxf(kmax, kmax_w[i]);
   const int64_t qrow0 = (int64_t)b * N;
-  const int tile0 = blockIdx.x * 4 * qtiles;
+  const int P = gridDim.x, ntile = (N + 31) / 32;
+  const int qtiles = (ntile - (int)blockIdx.x + P * kCrossWaves - 1 - P * w) / (P * kCrossWaves);  // this wave's
   auto qload = [&](int t, u32x4& qa, u32x4& qb, float& rq) {
-    const int n = min((tile0 + 4 * t + w) * 32 + ql, N - 1);
+    const int n = min(((int)blockIdx.x + P * (w + kCrossWaves * t)) * 32 + ql, N - 1);
     const uint16_t* qr = q + (qrow0 + n) * C + h * kHeadDim + 8 * hf;
     qa = load16(qr);
     qb = load16(qr + 16);
@@ -135,81 +150,105 @@ __global__ __launch_bounds__(256) void cross_attn_bf16(const uint16_t* __restric
   float rq;
   qload(0, qa, qb, rq);
   for (int t = 0; t < qtiles; ++t) {
-    const int n0 = (tile0 + 4 * t + w) * 32;
-    if (n0 >= N) break;  // uniform per wave; later tiles of this wave start further on
-    // q^ = bf16(q * r_q * gq); the next tile's loads go out now.
-    u32x4 qh[2];
+    const int n0 = ((int)blockIdx.x + P * (w + kCrossWaves * t)) * 32;
+    // q^ = bf16(q * r_q * gq) (the gains of this lane's dims 8hf..8hf+7 and 16+8hf..16+8hf+7 are read
+    // again per tile from the cache rather than held in registers); the next tile's loads go out now.
+    u32x4 qh[2] = {qa, qb};
+    if (NORM) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      qh[0][u] = NORM ? cvt_pk_bf16(bf16_lo(qa[u]) * rq * g[0][2 * u], bf16_hi(qa[u]) * rq * g[0][2 * u + 1]) : qa[u];
-      qh[1][u] = NORM ? cvt_pk_bf16(bf16_lo(qb[u]) * rq * g[1][2 * u], bf16_hi(qb[u]) * rq * g[1][2 * u + 1]) : qb[u];
+      for (int ks = 0; ks < 2; ++ks) {
+        const float* gp = gq + h * kHeadDim + 16 * ks + 8 * hf;
+        const f32x4 g0 = loadf4(gp), g1 = loadf4(gp + 4);
+        const float g[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+        const u32x4 x = ks ? qb : qa;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          qh[ks][u] = cvt_pk_bf16(bf16_lo(x[u]) * rq * g[2 * u], bf16_hi(x[u]) * rq * g[2 * u + 1]);
+      }
     }
     if (t + 1 < qtiles) qload(t + 1, qa, qb, rq);
 
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x16 o;
+    // Two passes over the keys, the logits formed on the MFMA both times (cheaper than keeping them):
+    // the first takes the row maximum, the second the exponentials, their sum and the value product,
+    // so no running rescale is needed.  Only the tile holding the last valid key is masked.  In both
+    // passes the next tile's logits are issued before this tile's vector work (two accumulator sets
+    // taken in turn), so the wave covers the MFMA latency itself.
+    const f32x16 zero = {};
+    auto logits = [&](int tt) {
+      const u32x4 a0 = load16(Ks + khat_off(32 * tt + ql, hf));
+      const u32x4 a1 = load16(Ks + khat_off(32 * tt + ql, 2 + hf));
+      f32x16 st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qh[0]), zero, 0, 0, 0);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), as_bf16x8(qh[1]), st, 0, 0, 0);
+      // st[r]: query n0 + ql, key 32 tt + 8 (r / 4) + 4 hf + r % 4 (logit before the scale sc)
+      if (32 * tt + 32 > kvl) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[r] = 0.f;
-    for (int ch = 0; ch < nchunks; ++ch) {
-      const int j0 = ch * kCrossChunk;
-      const int ntiles = min(kCrossChunk / 32, (kvl - j0 + 31) / 32);  // tiles holding a valid key
-      f32x16 s[kCrossChunk / 32];
-#pragma unroll
-      for (int tt = 0; tt < kCrossChunk / 32; ++tt) {
-        if (tt < ntiles) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[tt][r] = 0.f;
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const u32x4 a = load16(Ks + khat_off(j0 + 32 * tt + ql, 2 * ks + hf));
-            s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qh[ks]), s[tt], 0, 0, 0);
-          }
-        }
+        for (int r = 0; r < 16; ++r)
+          if (32 * tt + 8 * (r >> 2) + 4 * hf + (r & 3) >= kvl) st[r] = -INFINITY;
       }
-      // s[tt][r]: query n0 + ql, key j0 + 32 tt + 8 (r / 4) + 4 hf + r % 4 (logit before the scale sc).
-      float mc = -INFINITY;
+      return st;
+    };
+    // The constant subtracted before the exponential: softmax does not depend on it, and fp32 and bf16
+    // keep their relative precision over the whole exponent range, so any m >= every logit serves as
+    // long as it does not exceed them by so much that the weights leave the normal range.  By
+    // Cauchy-Schwarz m = |q^| max_j |k^_j| bounds every logit, and its overshoot is at most 2m; where
+    // sc * 2m <= 64 for every query of the tile (always with the norm at SANA's scales) that bound is
+    // used and the logits are formed once; otherwise a first pass takes the exact row maximum.
+    float qn = 0.f;
 #pragma unroll
-      for (int tt = 0; tt < kCrossChunk / 32; ++tt) {
-        if (tt < ntiles) {
+    for (int u = 0; u < 4; ++u) qn = dot2_bf16(qh[1][u], qh[1][u], dot2_bf16(qh[0][u], qh[0][u], qn));
+    qn += __shfl_xor(qn, 32);
+    float m = sqrtf(qn * kmax) * (1.0f + 0x1p-12f) + 0x1p-100f;
+    f32x16 s0, s1;
+    if (__ballot(sc * 2.f * m > 64.f) != 0) {  // uniform per wave
+      m = -INFINITY;
+      auto take_max = [&](const f32x16& st) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + 32 * tt + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (key >= kvl) s[tt][r] = -INFINITY;
-            mc = fmaxf(mc, s[tt][r]);
-          }
-        }
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, st[r]);
+      };
+      s0 = logits(0);
+      for (int tt = 0; tt < ktiles; tt += 2) {
+        if (tt + 1 < ktiles) s1 = logits(tt + 1);
+        take_max(s0);
+        if (tt + 2 < ktiles) s0 = logits(tt + 2);
+        if (tt + 1 < ktiles) take_max(s1);
       }
-      mc = fmaxf(mc, __shfl_xor(mc, 32));
-      const float m_new = fmaxf(m_run, mc);  // finite: the chunk holds a valid key
-      const float alpha = __builtin_amdgcn_exp2f(sc * (m_run - m_new));  // 0 for the first chunk
-      const float cm = -sc * m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[r] *= alpha;
-      m_run = m_new;
-#pragma unroll
-      for (int tt = 0; tt < kCrossChunk / 32; ++tt) {
-        if (tt < ntiles) {
-          uint32_t pk[8];
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[tt][r], sc, cm));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[tt][r + 1], sc, cm));
-            l_run += p0 + p1;
-            pk[r >> 1] = cvt_pk_bf16(p0, p1);
-          }
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int kb = j0 + 32 * tt + 16 * jj + 4 * hf;
-            const u32x2 a0 = *reinterpret_cast<const u32x2*>(Vt + ql * vpitch + kb);
-            const u32x2 a1 = *reinterpret_cast<const u32x2*>(Vt + ql * vpitch + kb + 8);
-            const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
-            const u32x4 bp = {pk[4 * jj], pk[4 * jj + 1], pk[4 * jj + 2], pk[4 * jj + 3]};
-            o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bp), o, 0, 0, 0);
-          }
-        }
-      }
+      m = fmaxf(m, __shfl_xor(m, 32));
     }
+    const float cm = -sc * m;  // finite when a key is valid
+    // The row sum is taken over the bf16-rounded weights the value product uses (v_dot2 against
+    // ones), in two halves for a shorter dependency chain.
+    float l0 = 0.f, l1 = 0.f;
+    constexpr uint32_t kOnes = 0x3f803f80u;  // two bf16 ones
+    f32x16 o = zero;
+    auto consume = [&](const f32x16& st, int tt) {
+      uint32_t pk[8];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2)
+        pk[r >> 1] = cvt_pk_bf16(__builtin_amdgcn_exp2f(fmaf(st[r], sc, cm)),
+                                 __builtin_amdgcn_exp2f(fmaf(st[r + 1], sc, cm)));
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        l0 = dot2_bf16(pk[i], kOnes, l0);
+        l1 = dot2_bf16(pk[i + 1], kOnes, l1);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int kb = 32 * tt + 16 * jj + 4 * hf;
+        const u32x2 a0 = *reinterpret_cast<const u32x2*>(Vt + ql * vpitch + kb);
+        const u32x2 a1 = *reinterpret_cast<const u32x2*>(Vt + ql * vpitch + kb + 8);
+        const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
+        const u32x4 bp = {pk[4 * jj], pk[4 * jj + 1], pk[4 * jj + 2], pk[4 * jj + 3]};
+        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bp), o, 0, 0, 0);
+      }
+    };
+    s0 = logits(0);
+    for (int tt = 0; tt < ktiles; tt += 2) {
+      if (tt + 1 < ktiles) s1 = logits(tt + 1);
+      consume(s0, tt);
+      if (tt + 2 < ktiles) s0 = logits(tt + 2);
+      if (tt + 1 < ktiles) consume(s1, tt + 1);
+    }
+    const float l_run = l0 + l1;
     // o[r]: dim 8 (r / 4) + 4 hf + r % 4 of query n0 + ql.
     const float lt = l_run + __shfl_xor(l_run, 32);
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
@@ -220,7 +259,7 @@ __global__ __launch_bounds__(256) void cross_attn_bf16(const uint16_t* __restric
       for (int gi = 0; gi < 4; ++gi) {
         const u32x2 pv = {cvt_pk_bf16(o[4 * gi] * inv, o[4 * gi + 1] * inv),
                           cvt_pk_bf16(o[4 * gi + 2] * inv, o[4 * gi + 3] * inv)};
-        __builtin_nontemporal_store(pv, reinterpret_cast<u32x2*>(orow + 8 * gi));
+        *reinterpret_cast<u32x2*>(orow + 8 * gi) = pv;  // ordinary stores: 8-26% faster than non-temporal
       }
     }
   }
@@ -249,19 +288,32 @@ hipError_t launch_cross_attn(const uint16_t* q, const uint16_t* k, const uint16_
   const uint16_t* kh = norm ? khat : k;
   const int Lp = (L + 31) / 32 * 32;
   const size_t lds = (size_t)Lp * 64 + (size_t)kHeadDim * (Lp + 4) * 2;
-  const int qtiles = N >= 8192 ? 4 : N >= 2048 ? 2 : 1;  // 32-query tiles per wave
-  const dim3 grid((unsigned)((N + 128 * qtiles - 1) / (128 * qtiles)), (unsigned)H, (unsigned)B);
+  // Blocks per (head, sample): as many as keep the grid resident at once (two 8-wave blocks per CU),
+  // at most one per 8 query tiles.
+  static std::atomic<int> cus_of[64];  // compute units per device, queried once
+  int dev = 0, num_cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    num_cus = cus_of[dev].load(std::memory_order_relaxed);
+    if (num_cus <= 0 && hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      cus_of[dev].store(num_cus, std::memory_order_relaxed);
+  }
+  if (num_cus <= 0) num_cus = 256;
+  const int64_t per_head = std::max<int64_t>(1, 2 * (int64_t)num_cus / ((int64_t)H * B));
+  const int P = (int)std::min<int64_t>(per_head, ((N + 31) / 32 + kCrossWaves - 1) / kCrossWaves);
+  const dim3 grid((unsigned)P, (unsigned)H, (unsigned)B);
   const void* kern = norm ? reinterpret_cast<const void*>(&cross_attn_bf16<true>)
                           : reinterpret_cast<const void*>(&cross_attn_bf16<false>);
-  const hipError_t ea = ensure_max_lds(kern, 160 * 1024);
+  // Dynamic LDS of up to 128.3 KB (1024 text tokens); the kernel's static LDS takes the rest of the
+  // 160 KB a block may use.
+  const hipError_t ea = ensure_max_lds(kern, 159 * 1024);
   if (ea != hipSuccess) return ea;
   final_launch();
   if (norm)
-    launch_kernel("cross_attn", cross_attn_bf16<true>, grid, 256, lds, stream, q, kh, v, r_q, gq, kv_len, N, L, Lp, H,
-                  qtiles, c, out);
+    launch_kernel("cross_attn", cross_attn_bf16<true>, grid, 64 * kCrossWaves, lds, stream, q, kh, v, r_q, gq, kv_len, N, L, Lp, H,
+                  c, out);
   else
-    launch_kernel("cross_attn", cross_attn_bf16<false>, grid, 256, lds, stream, q, kh, v, r_q, gq, kv_len, N, L, Lp, H,
-                  qtiles, c, out);
+    launch_kernel("cross_attn", cross_attn_bf16<false>, grid, 64 * kCrossWaves, lds, stream, q, kh, v, r_q, gq, kv_len, N, L, Lp, H,
+                  c, out);
   return hipGetLastError();
 }
 
