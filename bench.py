@@ -596,6 +596,23 @@ def main():
             log(f"[bench] config2: {scms * 1e3:.1f} us/step cold")
         secondary["kernels_us"] = {k: round(v * 1e3, 2) for k, v in kernel_times(sec_in, sanala).items()}
         del sec_in
+    cross = None
+    if not args.no_secondary and args.workload == "config4":
+        # The block's cross-attention over the same 4K latent (300 text tokens), warm, with its kernels.
+        x_in = Inputs("cross4k")
+        xms = time_steps(x_in, sanala, max(args.steps, 50), args.warmup)
+        xkt = kernel_times(x_in, sanala)
+        exps = float(x_in.N * int(x_in.kv_len.sum().item()) * x_in.H)
+        cms = xkt.get("cross_attn", float("nan"))
+        cross = {"workload": WORKLOADS["cross4k"]["desc"], "ms_per_step": round(xms, 5),
+                 "tokens_per_s": round(x_in.B * x_in.N / (xms * 1e-3), 1),
+                 "kernels_us": {k: round(v * 1e3, 2) for k, v in xkt.items()},
+                 "roofline": {"bound": "alu", "kernel": "cross_attn", "unit": "T exp2/s",
+                              "achieved": round(exps / (cms * 1e-3) / 1e12, 2), "peak": round(EXP2_PEAK_T, 2),
+                              "frac": round(exps / (cms * 1e-3) / 1e12 / EXP2_PEAK_T, 4)}}
+        log(f"[bench] cross4k: {xms * 1e3:.1f} us/step warm; kernels " +
+            ", ".join(f"{k}={v * 1e3:.1f}us" for k, v in xkt.items()))
+        del x_in
     ceiling = None
     if not args.no_cold:
         del flush
@@ -630,6 +647,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "secondary": secondary,
+        "cross_attention": cross,
         "source_hash": source_hash(),
     }
     print(json.dumps(line), flush=True)
