@@ -12,98 +12,131 @@
 
 namespace sanala {
 
-// Split-N KV partial state.  Block (c, h, b), 4 waves; the phi(K) and V rows of 64 tokens are staged in
-// LDS (the next 64 tokens' loads in flight while the current ones are summed), wave w takes tokens
-// w, w + 4, ... of them and lane l owns S[l/2][16*(l%2) .. 16*(l%2) + 15] and z[l/2] (fp32 FMAs in token
-// order); at the end the waves' sums are added in wave order.  With one chunk per sample (NC = 1) the
-// block writes S and z themselves, and no reduction launch follows.
+// Split-N KV partial state.  Block (c, h, b) of kF32StateWaves waves; the chunk is taken in sub-blocks
+// of 64 tokens whose phi(K) and V rows are staged in LDS (two buffers), with the loads of the next
+// kF32Ring sub-blocks in flight in registers, so a short chunk costs one memory round trip rather than
+// one per sub-block.  Wave w takes tokens w, w + W, ... of a sub-block; lane l owns the 4 x 4 block
+// S[4*(l/8) + i][4*(l%8) + j] and z[4*(l/8) + i], so a token costs each lane two 16-byte LDS reads
+// (four phi(k) values, four v values) for its 16 FMAs (fp32, in token order per element); at the end
+// the waves' sums are added in wave order.  With one chunk per sample (NC = 1) the block writes S and
+// z themselves, and no reduction launch follows.
+constexpr int kF32Ring = 4;
+constexpr int kF32StateWaves = 8;
 template <bool NORM>
-__global__ __launch_bounds__(256) void kv_partial_f32(const float* __restrict__ k, const float* __restrict__ v,
-                                                      int64_t ld, const float* __restrict__ r_k,
-                                                      const float* __restrict__ gk, int N, int H, int Tc, int NC,
-                                                      float* __restrict__ part, float* __restrict__ S32,
-                                                      float* __restrict__ zg) {
-  __shared__ float Kf[64][kHeadDim + 1];
-  __shared__ __attribute__((aligned(16))) float Vf[64][kHeadDim];
-  __shared__ __attribute__((aligned(16))) float red[3][kPartStride];
+__global__ __launch_bounds__(64 * kF32StateWaves) void kv_partial_f32(
+    const float* __restrict__ k, const float* __restrict__ v, int64_t ld, const float* __restrict__ r_k,
+    const float* __restrict__ gk, int N, int H, int Tc, int NC, float* __restrict__ part, float* __restrict__ S32,
+    float* __restrict__ zg) {
+  constexpr int R = kF32Ring;
+  constexpr int W = kF32StateWaves, NT = 64 * W, LD = 512 / NT;  // float4s of K (and of V) per thread
+  __shared__ __attribute__((aligned(16))) float Kf[2][64][kHeadDim];
+  __shared__ __attribute__((aligned(16))) float Vf[2][64][kHeadDim];
+  // wave w's sums: piece i of lane l (its S row 4*(l/8) + i) at 256*i + 4*l, z at 1024
+  __shared__ __attribute__((aligned(16))) float red[W - 1][kPartStride];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n_begin = c * Tc;
   const int n_end = min(N, n_begin + Tc);
+  const int nsub = n_end > n_begin ? (n_end - n_begin + 63) / 64 : 0;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int d = lane >> 1, e0 = 16 * (lane & 1);
+  const int d4 = 4 * (lane >> 3), e4 = 4 * (lane & 7);
   const int64_t row0 = (int64_t)b * N;
-  float acc[16];
+  float gg[4];  // the K gains of this thread's staging columns (the same for each of its float4s)
+#pragma unroll
+  for (int u = 0; u < 4; ++u) gg[u] = NORM ? gk[h * kHeadDim + (tid & 7) * 4 + u] : 1.f;
+  float acc[16];  // acc[4*i + j] = S[d4 + i][e4 + j]
 #pragma unroll
   for (int u = 0; u < 16; ++u) acc[u] = 0.f;
-  float zacc = 0.f;
-  f32x4 kv[2], vv[2];
-  float rr[2];
-  auto load = [&](int n0) {
+  float zacc[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x4 kv[R][LD], vv[R][LD];
+  float rr[R][LD];
+  // sub-block j of the chunk into ring slot s (rows past the chunk end: zeros)
+  auto load = [&](int s, int j) {
+    const int n0 = n_begin + 64 * j;
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int i = tid + it * 256;
+    for (int it = 0; it < LD; ++it) {
+      const int i = tid + it * NT;
       const int row = i >> 3, c4 = (i & 7) * 4;
       const int n = n0 + row;
-      kv[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-      vv[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-      rr[it] = 0.f;
+      kv[s][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      vv[s][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      rr[s][it] = 0.f;
       if (n < n_end) {
         const int64_t off = (row0 + n) * ld + h * kHeadDim + c4;
-        kv[it] = loadf4(k + off);
-        vv[it] = loadf4(v + off);
-        rr[it] = NORM ? r_k[row0 + n] : 1.f;
+        kv[s][it] = loadf4(k + off);
+        vv[s][it] = loadf4(v + off);
+        rr[s][it] = NORM ? r_k[row0 + n] : 1.f;
       }
     }
   };
-  if (n_begin < n_end) load(n_begin);
-  for (int n0 = n_begin; n0 < n_end; n0 += 64) {
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int i = tid + it * 256;
-      const int row = i >> 3, c4 = (i & 7) * 4;
+  for (int s = 0; s < R; ++s)
+    if (s < nsub) load(s, s);
+  for (int j0 = 0; j0 < nsub; j0 += R) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float gg = NORM ? gk[h * kHeadDim + c4 + u] : 1.f;
-        Kf[row][c4 + u] = fmaxf(NORM ? kv[it][u] * rr[it] * gg : kv[it][u], 0.f);  // rows past the end: 0
+    for (int s = 0; s < R; ++s) {
+      const int j = j0 + s;  // sub-block; buffer j % 2 = s % 2 (R is even)
+      if (j >= nsub) break;
+      const int bs = s & 1;
+#pragma unroll
+      for (int it = 0; it < LD; ++it) {
+        const int i = tid + it * NT;
+        const int row = i >> 3, c4 = (i & 7) * 4;
+        f32x4 kf;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          kf[u] = fmaxf(NORM ? kv[s][it][u] * rr[s][it] * gg[u] : kv[s][it][u], 0.f);  // rows past the end: 0
+        *reinterpret_cast<f32x4*>(&Kf[bs][row][c4]) = kf;
+        *reinterpret_cast<f32x4*>(&Vf[bs][row][c4]) = vv[s][it];
       }
-      *reinterpret_cast<f32x4*>(&Vf[row][c4]) = vv[it];
-    }
-    __syncthreads();
-    if (n0 + 64 < n_end) load(n0 + 64);
-    const int cnt = min(64, n_end - n0);
-    for (int t = w; t < cnt; t += 4) {
-      const float kd = Kf[t][d];
-      const f32x4* vr = reinterpret_cast<const f32x4*>(&Vf[t][e0]);
+      // One barrier per sub-block: buffer bs is written again two sub-blocks later, after every wave has
+      // passed the next sub-block's barrier and so finished reading it.
+      __syncthreads();
+      if (j + R < nsub) load(s, j + R);
+      const int cnt = min(64, n_end - (n_begin + 64 * j));
+#pragma unroll 4
+      for (int t = w; t < cnt; t += W) {
+        const f32x4 kq = *reinterpret_cast<const f32x4*>(&Kf[bs][t][d4]);
+        const f32x4 vq = *reinterpret_cast<const f32x4*>(&Vf[bs][t][e4]);
 #pragma unroll
-      for (int w4 = 0; w4 < 4; ++w4) {
-        const f32x4 vq = vr[w4];
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[4 * w4 + u] = fmaf(kd, vq[u], acc[4 * w4 + u]);
+          for (int jj = 0; jj < 4; ++jj) acc[4 * i + jj] = fmaf(kq[i], vq[jj], acc[4 * i + jj]);
+          zacc[i] += kq[i];
+        }
       }
-      zacc += kd;
     }
-    __syncthreads();
   }
-  // waves 1..3 hand their sums to wave 0, which adds them in wave order
+  // waves 1..W-1 hand their sums to wave 0, which adds them in wave order
   if (w > 0) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u) red[w - 1][d * kHeadDim + e0 + u] = acc[u];
-    if ((lane & 1) == 0) red[w - 1][kHeadDim * kHeadDim + d] = zacc;
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<f32x4*>(&red[w - 1][256 * i + 4 * lane]) =
+          f32x4{acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]};
+    if (e4 == 0)
+      *reinterpret_cast<f32x4*>(&red[w - 1][kHeadDim * kHeadDim + d4]) = f32x4{zacc[0], zacc[1], zacc[2], zacc[3]};
   }
   __syncthreads();
   if (w > 0) return;
 #pragma unroll
-  for (int u = 0; u < 16; ++u)
-    acc[u] = ((acc[u] + red[0][d * kHeadDim + e0 + u]) + red[1][d * kHeadDim + e0 + u]) + red[2][d * kHeadDim + e0 + u];
-  zacc = ((zacc + red[0][kHeadDim * kHeadDim + d]) + red[1][kHeadDim * kHeadDim + d]) + red[2][kHeadDim * kHeadDim + d];
+  for (int r = 0; r < W - 1; ++r) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 p = *reinterpret_cast<const f32x4*>(&red[r][256 * i + 4 * lane]);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) acc[4 * i + jj] += p[jj];
+    }
+    const f32x4 pz = *reinterpret_cast<const f32x4*>(&red[r][kHeadDim * kHeadDim + d4]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) zacc[i] += pz[i];
+  }
   const int64_t bh = (int64_t)b * H + h;
   float* Sd = NC == 1 ? S32 + bh * kHeadDim * kHeadDim : part + (bh * NC + c) * kPartStride;
   float* zd = NC == 1 ? zg + bh * kHeadDim : part + (bh * NC + c) * kPartStride + kHeadDim * kHeadDim;
 #pragma unroll
-  for (int w4 = 0; w4 < 4; ++w4)
-    *reinterpret_cast<f32x4*>(Sd + d * kHeadDim + e0 + 4 * w4) =
-        f32x4{acc[4 * w4], acc[4 * w4 + 1], acc[4 * w4 + 2], acc[4 * w4 + 3]};
-  if ((lane & 1) == 0) zd[d] = zacc;
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<f32x4*>(Sd + (d4 + i) * kHeadDim + e4) =
+        f32x4{acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]};
+  if (e4 == 0) *reinterpret_cast<f32x4*>(zd + d4) = f32x4{zacc[0], zacc[1], zacc[2], zacc[3]};
 }
 
 // One thread per state element: sum of the chunk partials in chunk order (deterministic).
@@ -120,20 +153,28 @@ __global__ __launch_bounds__(256) void kv_reduce_f32(const float* __restrict__ p
   else zg[bh * kHeadDim + (i - kHeadDim * kHeadDim)] = s;
 }
 
-// Output.  Block = 16 tokens x 8 heads (blockIdx.z picks the head group); S and z of the group and the
-// block's phi(Q) rows are staged in LDS (phi(q) = ReLU(q * r_q * gq), r_q from the row-statistics
-// launch).  Thread (t, h, half) forms output channels 16*half .. 16*half + 15 of token t, head h:
-// num_e = sum_d phi_d S[d][e] and den = sum_d phi_d z[d], both fp32 FMAs in order d = 0..31, then
-// num / (den + eps).
-constexpr int kF32OutHeads = 8;
+// Output.  Block = 16 tokens x 4 heads (blockIdx.z picks the head group), so that even a 256-token
+// sample spreads over a few hundred blocks; S and z of the group and the block's phi(Q) rows are staged
+// in LDS (phi(q) = ReLU(q * r_q * gq), r_q from the row-statistics launch).  Thread (t, h, qtr) forms
+// output channels 8*qtr .. 8*qtr + 7 of token t, head h: num_e = sum_d phi_d S[d][e] and
+// den = sum_d phi_d z[d], both fp32 FMAs in order d = 0..31, then num / (den + eps).
+//
+// LDS layout of S: head h at word h * kF32HeadStride, row d at d * 32 within it, and within a row the
+// 16-byte piece w (0, 1) of quarter qtr at word 16*w + 4*qtr.  The 16 lanes that read together (one
+// token, 4 heads x 4 quarters) then touch 64 distinct banks: the head stride is 16 words past a multiple
+// of 64 and the quarters' pieces are interleaved.  (A plain [h][d][e] layout put all heads of a read on
+// the same banks.)
+constexpr int kF32OutHeads = 4;
+constexpr int kF32HeadStride = kHeadDim * kHeadDim + 16;
 template <bool NORM>
 __global__ __launch_bounds__(256) void out_f32(const float* __restrict__ q, int64_t ldq, const float* __restrict__ gq,
                                                const float* __restrict__ r_q, const float* __restrict__ S32,
                                                const float* __restrict__ zg, int N, int H, float eps,
                                                float* __restrict__ out, int64_t ldo) {
   constexpr int HG = kF32OutHeads;
-  __shared__ __attribute__((aligned(16))) float Ss[HG][kHeadDim][kHeadDim];
-  __shared__ float Zs[HG][kHeadDim];
+  constexpr int GC = HG * kHeadDim;  // channels of the group
+  __shared__ __attribute__((aligned(16))) float Ss[HG * kF32HeadStride];
+  __shared__ float Zs[HG][kHeadDim + 1];
   __shared__ float Ps[16][HG][kHeadDim + 1];
   const int b = blockIdx.y, n0 = blockIdx.x * 16, hg0 = blockIdx.z * HG;
   const int nh = min(HG, H - hg0);
@@ -141,28 +182,33 @@ __global__ __launch_bounds__(256) void out_f32(const float* __restrict__ q, int6
   const int64_t row0 = (int64_t)b * N;
   const int64_t bh0 = (int64_t)b * H + hg0;
   // S, z of the group and phi(Q) of the tile: all loads of a thread issued before its LDS stores.
-  f32x4 sreg[HG], qreg[4];
-  float zreg = 0.f, rq[4];
+  constexpr int SJ = HG * kHeadDim * kHeadDim / 4 / 256;  // float4s of S per thread
+  constexpr int QJ = 16 * GC / 4 / 256;                   // float4s of Q per thread
+  f32x4 sreg[SJ], qreg[QJ];
+  float zreg = 0.f, rq[QJ];
 #pragma unroll
-  for (int j = 0; j < HG; ++j) {
+  for (int j = 0; j < SJ; ++j) {
     const int i = tid + 256 * j;  // float4 index into the group's S (256 per head)
     sreg[j] = i < nh * 256 ? loadf4(S32 + bh0 * kHeadDim * kHeadDim + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   if (tid < nh * kHeadDim) zreg = zg[bh0 * kHeadDim + tid];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {  // float4 i: token i / 64, channels 4 * (i % 64) .. of the group's 256
-    const int i = tid + 256 * j, t = i >> 6, c4 = 4 * (i & 63);
+  for (int j = 0; j < QJ; ++j) {  // float4 i: token i / 32, channels 4 * (i % 32) .. of the group's 128
+    const int i = tid + 256 * j, t = i >> 5, c4 = 4 * (i & 31);
     const int n = n0 + t;
     const bool ok = n < N && c4 < nh * kHeadDim;
     qreg[j] = ok ? loadf4(q + (row0 + n) * ldq + hg0 * kHeadDim + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
     rq[j] = (NORM && ok) ? r_q[row0 + n] : 1.f;
   }
 #pragma unroll
-  for (int j = 0; j < HG; ++j) reinterpret_cast<f32x4*>(&Ss[0][0][0])[tid + 256 * j] = sreg[j];
+  for (int j = 0; j < SJ; ++j) {
+    const int i = tid + 256 * j, hl = i >> 8, d = (i >> 3) & 31, e4 = i & 7;  // e = 4 * e4 = 8*qtr + 4*w
+    *reinterpret_cast<f32x4*>(&Ss[hl * kF32HeadStride + d * kHeadDim + 16 * (e4 & 1) + 4 * (e4 >> 1)]) = sreg[j];
+  }
   if (tid < HG * kHeadDim) Zs[tid / kHeadDim][tid % kHeadDim] = zreg;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = tid + 256 * j, t = i >> 6, c4 = 4 * (i & 63);
+  for (int j = 0; j < QJ; ++j) {
+    const int i = tid + 256 * j, t = i >> 5, c4 = 4 * (i & 31);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int cc = c4 + u;
@@ -171,31 +217,31 @@ __global__ __launch_bounds__(256) void out_f32(const float* __restrict__ q, int6
     }
   }
   __syncthreads();
-  const int t = tid >> 4, hl = (tid >> 1) & 7, half = tid & 1;
+  const int t = tid >> 4, hl = (tid >> 2) & 3, qtr = tid & 3;
   const int n = n0 + t;
   if (n >= N || hl >= nh) return;
-  float num[16];
+  float num[8];
 #pragma unroll
-  for (int u = 0; u < 16; ++u) num[u] = 0.f;
+  for (int u = 0; u < 8; ++u) num[u] = 0.f;
   float den = 0.f;
-#pragma unroll 4
+  const f32x4* srow = reinterpret_cast<const f32x4*>(&Ss[hl * kF32HeadStride + 4 * qtr]);
+#pragma unroll 8
   for (int dd = 0; dd < kHeadDim; ++dd) {
     const float pq = Ps[t][hl][dd];
-    const f32x4* srow = reinterpret_cast<const f32x4*>(&Ss[hl][dd][16 * half]);
 #pragma unroll
-    for (int w4 = 0; w4 < 4; ++w4) {
-      const f32x4 sv = srow[w4];
+    for (int w = 0; w < 2; ++w) {
+      const f32x4 sv = srow[dd * (kHeadDim / 4) + 4 * w];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) num[4 * w4 + u] = fmaf(pq, sv[u], num[4 * w4 + u]);
+      for (int u = 0; u < 4; ++u) num[4 * w + u] = fmaf(pq, sv[u], num[4 * w + u]);
     }
     den = fmaf(pq, Zs[hl][dd], den);
   }
   const float dv = den + eps;
-  float* o = out + (row0 + n) * ldo + (hg0 + hl) * kHeadDim + 16 * half;
+  float* o = out + (row0 + n) * ldo + (hg0 + hl) * kHeadDim + 8 * qtr;
 #pragma unroll
-  for (int w4 = 0; w4 < 4; ++w4)
-    *reinterpret_cast<f32x4*>(o + 4 * w4) =
-        f32x4{num[4 * w4] / dv, num[4 * w4 + 1] / dv, num[4 * w4 + 2] / dv, num[4 * w4 + 3] / dv};
+  for (int w = 0; w < 2; ++w)
+    *reinterpret_cast<f32x4*>(o + 4 * w) =
+        f32x4{num[4 * w] / dv, num[4 * w + 1] / dv, num[4 * w + 2] / dv, num[4 * w + 3] / dv};
 }
 
 hipError_t launch_attn_f32(const AttnPlan& p, const float* q, int64_t ldq, const float* k, const float* v,
@@ -214,10 +260,10 @@ hipError_t launch_attn_f32(const AttnPlan& p, const float* q, int64_t ldq, const
                   C, eps, r_k, q, ldq, r_q);
   const dim3 grid(p.NC, H, B);
   if (p.norm)
-    launch_kernel("kv_partial", kv_partial_f32<true>, grid, 256, 0, stream, k, v, ldkv, r_k, gk, N, H, p.Tc, p.NC,
+    launch_kernel("kv_partial", kv_partial_f32<true>, grid, 64 * kF32StateWaves, 0, stream, k, v, ldkv, r_k, gk, N, H, p.Tc, p.NC,
                   part, S32, z);
   else
-    launch_kernel("kv_partial", kv_partial_f32<false>, grid, 256, 0, stream, k, v, ldkv, nullptr, nullptr, N, H, p.Tc,
+    launch_kernel("kv_partial", kv_partial_f32<false>, grid, 64 * kF32StateWaves, 0, stream, k, v, ldkv, nullptr, nullptr, N, H, p.Tc,
                   p.NC, part, S32, z);
   if (p.NC > 1) {
     const int64_t elems = (int64_t)B * H * kPartStride;
