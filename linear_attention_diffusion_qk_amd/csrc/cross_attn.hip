@@ -36,6 +36,7 @@ constexpr int kCrossWaves = 8;      // waves per cross_attn block: they share on
 constexpr int kCrossPrepUnits = 8;  // 16-byte units per lane in cross_prep: rows of up to 4096 channels
 constexpr float kLog2e = 1.4426950408889634f;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 // Byte offset of 16-byte unit u (dims 8u..8u+7) of key j in the staged k^ tile (64-byte rows).  The
 // XOR with bits 2-3 of j puts the same unit of any 16 consecutive keys in 16 different bank slots.
@@ -155,6 +156,7 @@ __global__ __launch_bounds__(64 * kCrossWaves, 4) void cross_attn_bf16(const uin
     // again per tile from the cache rather than held in registers); the next tile's loads go out now.
     u32x4 qh[2] = {qa, qb};
     if (NORM) {
+      rq *= sc;  // the softmax scale rides on the one rounding q^ takes anyway
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const float* gp = gq + h * kHeadDim + 16 * ks + 8 * hf;
@@ -168,18 +170,31 @@ __global__ __launch_bounds__(64 * kCrossWaves, 4) void cross_attn_bf16(const uin
     }
     if (t + 1 < qtiles) qload(t + 1, qa, qb, rq);
 
-    // Two passes over the keys, the logits formed on the MFMA both times (cheaper than keeping them):
-    // the first takes the row maximum, the second the exponentials, their sum and the value product,
-    // so no running rescale is needed.  Only the tile holding the last valid key is masked.  In both
-    // passes the next tile's logits are issued before this tile's vector work (two accumulator sets
-    // taken in turn), so the wave covers the MFMA latency itself.
+    // The logits are formed on the MFMA; the next tile's logits are issued before this tile's vector
+    // work (two accumulator sets taken in turn), so the wave covers the MFMA latency itself.  Only the
+    // tile holding the last valid key is masked.
+    //
+    // With the norm on, q^ carries the scale sc, and the constant the softmax subtracts is added on the
+    // MFMA too: a product of a ones column of the keys with (-m_hi, -m_lo) in the queries' first two
+    // slots (32x32x8, m = m_hi + m_lo to 2^-17 relative, the same for every key of a query) adds -m to
+    // each logit, so a weight is exp2 of the accumulator itself.  Without the norm q and k are used as
+    // given, so folding the scale into a bf16 operand would add a rounding the logits do not otherwise
+    // take: there the scale and the constant are applied in fp32 by one FMA per logit.
     const f32x16 zero = {};
+    const i16x4 kone = {(short)(hf == 0 ? 0x3f80 : 0), (short)(hf == 0 ? 0x3f80 : 0), 0, 0};  // A[key][0..1] = 1
+    i16x4 qbias = {0, 0, 0, 0};
     auto logits = [&](int tt) {
       const u32x4 a0 = load16(Ks + khat_off(32 * tt + ql, hf));
       const u32x4 a1 = load16(Ks + khat_off(32 * tt + ql, 2 + hf));
-      f32x16 st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qh[0]), zero, 0, 0, 0);
+      f32x16 st;
+      if constexpr (NORM) {
+        st = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(kone, qbias, zero, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qh[0]), st, 0, 0, 0);
+      } else {
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qh[0]), zero, 0, 0, 0);
+      }
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), as_bf16x8(qh[1]), st, 0, 0, 0);
-      // st[r]: query n0 + ql, key 32 tt + 8 (r / 4) + 4 hf + r % 4 (logit before the scale sc)
+      // st[r]: query n0 + ql, key 32 tt + 8 (r / 4) + 4 hf + r % 4
       if (32 * tt + 32 > kvl) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -191,15 +206,17 @@ __global__ __launch_bounds__(64 * kCrossWaves, 4) void cross_attn_bf16(const uin
     // keep their relative precision over the whole exponent range, so any m >= every logit serves as
     // long as it does not exceed them by so much that the weights leave the normal range.  By
     // Cauchy-Schwarz m = |q^| max_j |k^_j| bounds every logit, and its overshoot is at most 2m; where
-    // sc * 2m <= 64 for every query of the tile (always with the norm at SANA's scales) that bound is
-    // used and the logits are formed once; otherwise a first pass takes the exact row maximum.
+    // 2m <= 64 in exponent units for every query of the tile (always with the norm at SANA's scales)
+    // that bound is used and the logits are formed once; otherwise a first pass takes the exact row
+    // maximum.
     float qn = 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) qn = dot2_bf16(qh[1][u], qh[1][u], dot2_bf16(qh[0][u], qh[0][u], qn));
     qn += __shfl_xor(qn, 32);
     float m = sqrtf(qn * kmax) * (1.0f + 0x1p-12f) + 0x1p-100f;
+    const float scl = NORM ? 1.f : sc;  // scale still to apply to an accumulator value
     f32x16 s0, s1;
-    if (__ballot(sc * 2.f * m > 64.f) != 0) {  // uniform per wave
+    if (__ballot(scl * 2.f * m > 64.f) != 0) {  // uniform per wave
       m = -INFINITY;
       auto take_max = [&](const f32x16& st) {
 #pragma unroll
@@ -213,8 +230,14 @@ __global__ __launch_bounds__(64 * kCrossWaves, 4) void cross_attn_bf16(const uin
         if (tt + 1 < ktiles) take_max(s1);
       }
       m = fmaxf(m, __shfl_xor(m, 32));
+      if (!(m > -INFINITY)) m = 0.f;  // no valid key: every weight is zero anyway
     }
-    const float cm = -sc * m;  // finite when a key is valid
+    if constexpr (NORM) {
+      const uint32_t hi = f32_to_bf16_bits(-m) & 0xffffu;
+      const uint32_t lo = f32_to_bf16_bits(-m - __uint_as_float(hi << 16)) & 0xffffu;
+      qbias = {(short)(hf == 0 ? hi : 0u), (short)(hf == 0 ? lo : 0u), 0, 0};
+    }
+    const float cm = -scl * m;  // the fp32 path's constant
     // The row sum is taken over the bf16-rounded weights the value product uses (v_dot2 against
     // ones), in two halves for a shorter dependency chain.
     float l0 = 0.f, l1 = 0.f;
@@ -223,9 +246,13 @@ __global__ __launch_bounds__(64 * kCrossWaves, 4) void cross_attn_bf16(const uin
     auto consume = [&](const f32x16& st, int tt) {
       uint32_t pk[8];
 #pragma unroll
-      for (int r = 0; r < 16; r += 2)
-        pk[r >> 1] = cvt_pk_bf16(__builtin_amdgcn_exp2f(fmaf(st[r], sc, cm)),
-                                 __builtin_amdgcn_exp2f(fmaf(st[r + 1], sc, cm)));
+      for (int r = 0; r < 16; r += 2) {
+        if constexpr (NORM)
+          pk[r >> 1] = cvt_pk_bf16(__builtin_amdgcn_exp2f(st[r]), __builtin_amdgcn_exp2f(st[r + 1]));
+        else
+          pk[r >> 1] = cvt_pk_bf16(__builtin_amdgcn_exp2f(fmaf(st[r], scl, cm)),
+                                   __builtin_amdgcn_exp2f(fmaf(st[r + 1], scl, cm)));
+      }
 #pragma unroll
       for (int i = 0; i < 8; i += 2) {
         l0 = dot2_bf16(pk[i], kOnes, l0);
