@@ -12,17 +12,18 @@
 //               takes 32 queries at a time: q^ = bf16(q * r_q * gq) in registers, S^T = k^ q^T on
 //               v_mfma_f32_32x32x16_bf16, so that a lane holds one query's logits for 16 of every 32
 //               keys and the softmax's max and sum are in-lane plus one exchange between the two lane
-//               halves.  The logits stay exact products of the bf16 operands (fp32 sums); the softmax
-//               scale log2(e)/sqrt(D) is applied in fp32 inside the exponent's multiply-add, since
-//               folding it into bf16 keys would round logits of a few hundred (no norm) by a whole unit.
-//               The softmax here costs more vector-ALU work per logit (a quarter-rate exp2 among about
-//               six operations) than the MFMA work, so the logits are formed twice rather than kept:
-//               one pass for the row maximum, one for P = exp2(sc (s - max)), its sum and the value
-//               product.  P is rounded to bf16 (its row sum taken over those rounded values) and
-//               O^T = V^T P^T runs on the same MFMA with P taken
-//               straight from the S^T registers: the MFMA's k index runs over the keys in the order the
-//               accumulator holds them (lane half g: keys 4g..4g+3 and 8+4g..8+4g+3 of each 16), and V^T
-//               is read from LDS in that order.  o = O / sum, stored as bf16.
+//               halves.  The logits are exact products of the bf16 operands (fp32 sums).  With the
+//               norm on, q^ carries the softmax scale log2(e)/sqrt(D) (one rounding either way) and
+//               the subtracted constant m is added on the MFMA, so P = exp2 of the accumulator; without
+//               it q and k are used as given, and the scale and m are applied in fp32 by one FMA per
+//               logit (folding the scale into a bf16 operand would round logits of a few hundred by a
+//               whole unit).  m is the Cauchy-Schwarz bound |q^| max|k^| where that keeps the weights
+//               in range, else the exact row maximum from a first pass over the keys (the logits are
+//               formed again rather than kept).  P is rounded to bf16 (its row sum taken over those
+//               rounded values) and O^T = V^T P^T runs on the same MFMA with P taken straight from the
+//               S^T registers: the MFMA's k index runs over the keys in the order the accumulator holds
+//               them (lane half g: keys 4g..4g+3 and 8+4g..8+4g+3 of each 16), and V^T is read from LDS
+//               in that order.  o = O / sum, stored as bf16.
 #include "common.h"
 
 #include <algorithm>
