@@ -244,30 +244,32 @@ __global__ __launch_bounds__(64 * kCrossWaves, 4) void cross_attn_bf16(const uin
     float l0 = 0.f, l1 = 0.f;
     constexpr uint32_t kOnes = 0x3f803f80u;  // two bf16 ones
     f32x16 o = zero;
-    auto consume = [&](const f32x16& st, int tt) {
-      uint32_t pk[8];
+    // Half jj of a key tile: keys 16 jj .. 16 jj + 15 (accumulator entries 8 jj .. 8 jj + 7).
+    auto consume_half = [&](const f32x16& st, int tt, int jj) {
+      uint32_t pk[4];
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
+      for (int r = 8 * jj; r < 8 * jj + 8; r += 2) {
         if constexpr (NORM)
-          pk[r >> 1] = cvt_pk_bf16(__builtin_amdgcn_exp2f(st[r]), __builtin_amdgcn_exp2f(st[r + 1]));
+          pk[(r >> 1) & 3] = cvt_pk_bf16(__builtin_amdgcn_exp2f(st[r]), __builtin_amdgcn_exp2f(st[r + 1]));
         else
-          pk[r >> 1] = cvt_pk_bf16(__builtin_amdgcn_exp2f(fmaf(st[r], scl, cm)),
-                                   __builtin_amdgcn_exp2f(fmaf(st[r + 1], scl, cm)));
+          pk[(r >> 1) & 3] = cvt_pk_bf16(__builtin_amdgcn_exp2f(fmaf(st[r], scl, cm)),
+                                         __builtin_amdgcn_exp2f(fmaf(st[r + 1], scl, cm)));
       }
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        l0 = dot2_bf16(pk[i], kOnes, l0);
-        l1 = dot2_bf16(pk[i + 1], kOnes, l1);
-      }
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int kb = 32 * tt + 16 * jj + 4 * hf;
-        const u32x2 a0 = *reinterpret_cast<const u32x2*>(Vt + ql * vpitch + kb);
-        const u32x2 a1 = *reinterpret_cast<const u32x2*>(Vt + ql * vpitch + kb + 8);
-        const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
-        const u32x4 bp = {pk[4 * jj], pk[4 * jj + 1], pk[4 * jj + 2], pk[4 * jj + 3]};
-        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bp), o, 0, 0, 0);
-      }
+      l0 = dot2_bf16(pk[0], kOnes, l0);
+      l1 = dot2_bf16(pk[1], kOnes, l1);
+      l0 = dot2_bf16(pk[2], kOnes, l0);
+      l1 = dot2_bf16(pk[3], kOnes, l1);
+      const int kb = 32 * tt + 16 * jj + 4 * hf;
+      const u32x2 a0 = *reinterpret_cast<const u32x2*>(Vt + ql * vpitch + kb);
+      const u32x2 a1 = *reinterpret_cast<const u32x2*>(Vt + ql * vpitch + kb + 8);
+      const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
+      const u32x4 bp = {pk[0], pk[1], pk[2], pk[3]};
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bp), o, 0, 0, 0);
+    };
+    // The upper half of the tile holding the last valid key is skipped when it holds none.
+    auto consume = [&](const f32x16& st, int tt) {
+      consume_half(st, tt, 0);
+      if (32 * tt + 16 < kvl) consume_half(st, tt, 1);
     };
     s0 = logits(0);
     for (int tt = 0; tt < ktiles; tt += 2) {
