@@ -222,6 +222,33 @@ def time_steady(inputs: Inputs, sanala, steps: int, settle_s: float = 0.2) -> fl
     return e0.elapsed_time(e1) / steps
 
 
+def pct(xs, q: float) -> float:
+    """q-quantile of xs (linear interpolation between order statistics)."""
+    v = sorted(xs)
+    pos = q * (len(v) - 1)
+    lo = int(pos)
+    hi = min(lo + 1, len(v) - 1)
+    return v[lo] + (v[hi] - v[lo]) * (pos - lo)
+
+
+def spread(us) -> dict:
+    return {"median": round(pct(us, 0.5), 2), "p10": round(pct(us, 0.1), 2), "p90": round(pct(us, 0.9), 2)}
+
+
+def time_rounds(inputs: Inputs, sanala, rounds: int = 20, per: int = 10) -> list:
+    """us per call in each of `rounds` rounds of `per` back-to-back calls (one event pair per round, so no
+    event packets sit between the calls; run after time_steady, with settled clocks)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(rounds)]
+    for e0, e1 in evs:
+        e0.record()
+        for _ in range(per):
+            inputs.step(sanala)
+        e1.record()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) / per * 1e3 for e0, e1 in evs]
+
+
 class CacheFlush:
     """A read-only pass over 1 GiB between timed calls: evicts the L2s and the 256 MB Infinity Cache and
     leaves only clean lines behind (a write pass would leave dirty lines whose write-back lands on the
@@ -237,8 +264,8 @@ class CacheFlush:
         torch.sum(self.buf, dim=0, out=self.sink)
 
 
-def time_cold(inputs: Inputs, sanala, steps: int, warmup: int, flush: CacheFlush) -> float:
-    """ms per call with the caches flushed before every call (flush outside the events): the inputs
+def time_cold(inputs: Inputs, sanala, steps: int, warmup: int, flush: CacheFlush):
+    """(mean ms per call, us of each call) with the caches flushed before every call (flush outside the events): the inputs
     come from HBM, as when the call follows unrelated work."""
     import torch
     for _ in range(warmup):
@@ -252,7 +279,8 @@ def time_cold(inputs: Inputs, sanala, steps: int, warmup: int, flush: CacheFlush
         inputs.step(sanala)
         e1.record()
     torch.cuda.synchronize()
-    return sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+    times = [e0.elapsed_time(e1) for e0, e1 in evs]
+    return sum(times) / steps, [t * 1e3 for t in times]
 
 
 def copy_ceiling(reps: int = 20):
@@ -552,14 +580,17 @@ def main():
         steady = point(main_in, sts)
         steady["note"] = ("back-to-back calls after 0.2 s of calls, once the clocks have settled; value above: "
                           "the contract's warm-up steps, then the timed steps")
+        steady["per_call_us"] = spread(time_rounds(main_in, sanala))
+        steady["per_call_us"]["note"] = "over 20 rounds of 10 back-to-back calls (one event pair per round)"
         log(f"[bench] {args.workload} steady state: {sts * 1e3:.1f} us/step")
     cold = None
     flush = None
     if not args.no_cold and main_in.kind in ("attn", "qkv", "w8a8", "cross"):
         flush = CacheFlush()
-        cms = time_cold(main_in, sanala, args.steps, max(1, args.warmup // 2), flush)
+        cms, cold_us = time_cold(main_in, sanala, args.steps, max(1, args.warmup // 2), flush)
         cold = point(main_in, cms)
         cold["note"] = "1 GiB read-only pass before every call, outside the events"
+        cold["per_call_us"] = spread(cold_us)
         log(f"[bench] {args.workload} cold: {cms * 1e3:.1f} us/step")
 
     kt = kernel_times(main_in, sanala)
@@ -620,11 +651,13 @@ def main():
         ssts = time_steady(sec_in, sanala, 500)
         secondary["steady"] = point(sec_in, ssts)
         secondary["steady"]["note"] = "back-to-back calls after 0.2 s of calls (settled clocks)"
+        secondary["steady"]["per_call_us"] = spread(time_rounds(sec_in, sanala))
         log(f"[bench] config2: {ssts * 1e3:.1f} us/step steady state")
         if flush is not None:
-            scms = time_cold(sec_in, sanala, max(args.steps, 50), args.warmup, flush)
+            scms, scold_us = time_cold(sec_in, sanala, max(args.steps, 50), args.warmup, flush)
             secondary["cold"] = point(sec_in, scms)
             secondary["cold"]["note"] = "1 GiB read-only pass before every call, outside the events: inputs from HBM"
+            secondary["cold"]["per_call_us"] = spread(scold_us)
             log(f"[bench] config2: {scms * 1e3:.1f} us/step cold")
         secondary["kernels_us"] = {k: round(v * 1e3, 2) for k, v in kernel_times(sec_in, sanala).items()}
         del sec_in
