@@ -10,8 +10,8 @@ Eq. (1), with one eps inside the QK-Norm square root and one after the denominat
   denominator: the output kernels' eps / r_q = eps * sqrt(ms + eps) rewrite and the state's r_k are
   then far from their small-eps values.
 * eps = 0 with an all-zero phi(q) row: 0/0, NaN on both sides, at the same positions.
-* The widest head count the library takes (H = 320) on the fp32 path (160 KB of LDS in its output
-  kernel) and on the 16-bit path.
+* The widest head count the library takes (H = 320) on the fp32 path (80 head groups of 4 in its output
+  kernel's grid) and on the 16-bit path.
 """
 import os
 
