@@ -173,7 +173,8 @@ __global__ __launch_bounds__(64 * kCrossWaves, 4) void cross_attn_bf16(const uin
 
     // The logits are formed on the MFMA; the next tile's logits are issued before this tile's vector
     // work (two accumulator sets taken in turn), so the wave covers the MFMA latency itself.  Only the
-    // tile holding the last valid key is masked.
+    // tile holding the last valid key is masked.  A wave raises its issue priority while it issues
+    // MFMAs (s_setprio), so that the matrix core of its SIMD is fed ahead of the other waves' vector work.
     //
     // With the norm on, q^ carries the scale sc, and the constant the softmax subtracts is added on the
     // MFMA too: a product of a ones column of the keys with (-m_hi, -m_lo) in the queries' first two
@@ -188,6 +189,7 @@ __global__ __launch_bounds__(64 * kCrossWaves, 4) void cross_attn_bf16(const uin
       const u32x4 a0 = load16(Ks + khat_off(32 * tt + ql, hf));
       const u32x4 a1 = load16(Ks + khat_off(32 * tt + ql, 2 + hf));
       f32x16 st;
+      __builtin_amdgcn_s_setprio(1);
       if constexpr (NORM) {
         st = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(kone, qbias, zero, 0, 0, 0);
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qh[0]), st, 0, 0, 0);
@@ -195,6 +197,7 @@ __global__ __launch_bounds__(64 * kCrossWaves, 4) void cross_attn_bf16(const uin
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qh[0]), zero, 0, 0, 0);
       }
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), as_bf16x8(qh[1]), st, 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
       // st[r]: query n0 + ql, key 32 tt + 8 (r / 4) + 4 hf + r % 4
       if (32 * tt + 32 > kvl) {
 #pragma unroll
@@ -264,7 +267,9 @@ __global__ __launch_bounds__(64 * kCrossWaves, 4) void cross_attn_bf16(const uin
       const u32x2 a1 = *reinterpret_cast<const u32x2*>(Vt + ql * vpitch + kb + 8);
       const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
       const u32x4 bp = {pk[0], pk[1], pk[2], pk[3]};
+      __builtin_amdgcn_s_setprio(1);
       o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bp), o, 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
     };
     // The upper half of the tile holding the last valid key is skipped when it holds none.
     auto consume = [&](const f32x16& st, int tt) {
