@@ -335,12 +335,18 @@ def host_cpu() -> dict:
     return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "usable_cpus": affinity}
 
 
-def kernel_times(inputs: Inputs, sanala, reps: int = 20):
-    """Average per-kernel duration from the start/stop events of each kernel's own dispatch (library timing)."""
-    sanala.sana_timing_enable(True)
+def kernel_times(inputs: Inputs, sanala, reps: int = 20, lead: int = 4):
+    """Average per-kernel duration from the start/stop events of each kernel's own dispatch (library timing).
+    Each timed call is queued behind `lead` untimed ones, so that it runs on a busy GPU as the calls of a
+    back-to-back run do (reading a call's events waits for it, which would otherwise leave the GPU idle
+    before every timed call)."""
     acc = {}
     try:
         for _ in range(reps):
+            sanala.sana_timing_enable(False)
+            for _ in range(lead):
+                inputs.step(sanala)
+            sanala.sana_timing_enable(True)
             inputs.step(sanala)
             for name, ms in sanala.sana_timing_last():
                 acc.setdefault(name, []).append(ms)
