@@ -32,6 +32,27 @@ def test_head_counts(gpu_lib, H):
         check(run_attn(gpu_lib, inp), oracle_out(inp), inp.v, dtype, f"H={H}")
 
 
+@pytest.mark.parametrize("N,chunk", [(5000, None), (3000, "1024")], ids=["planner", "chunk1024"])
+def test_fp32_state_over_long_chunks(gpu_lib, N, chunk):
+    """The fp32 state kernel keeps four 64-token sub-blocks' loads in flight in a ring of register sets;
+    chunks of more than four sub-blocks reuse its slots (5000 tokens: the planner's chunks of 384, six
+    sub-blocks; SANA_KV_CHUNK=1024: sixteen)."""
+    import os
+    inp = gen_attn(2100 + N, 1, N, dtype="f32")
+    old = os.environ.get("SANA_KV_CHUNK")
+    if chunk is not None:
+        os.environ["SANA_KV_CHUNK"] = chunk
+    try:
+        o = run_attn(gpu_lib, inp)
+    finally:
+        if chunk is not None:
+            if old is None:
+                del os.environ["SANA_KV_CHUNK"]
+            else:
+                os.environ["SANA_KV_CHUNK"] = old
+    check(o, oracle_out(inp), inp.v, "f32", f"fp32 N={N} chunk={chunk}")
+
+
 def test_config1_fp32_full(gpu_lib):
     inp = gen_config(1)
     check(run_attn(gpu_lib, inp), oracle_out(inp), inp.v, "f32", "config1")
