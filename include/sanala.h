@@ -206,9 +206,11 @@ sana_status_t sana_mix_ffn_fwd(const void* x, const void* W1, const void* Wdw, c
  *   dtype    SANA_BF16 (others: SANA_ERR_UNSUPPORTED).
  *
  * Arithmetic: fp32 statistics; with the norm the keys enter the MFMA as bf16(k * r_k * gk) and the
- * queries as bf16(q * r_q * gq) (without it, as given); logits as fp32 sums of the exact bf16 products,
- * the 1/sqrt(D) scale and the softmax in fp32 (exp2), the softmax weights rounded to bf16 for the value
- * product, fp32 accumulation, bf16 output (round to nearest even).
+ * queries as bf16(q * r_q * gq * log2(e)/sqrt(D)) (the softmax scale taken into that one rounding), and
+ * the subtracted constant is added on the MFMA as a bf16 pair; without the norm q and k enter as given
+ * and the scale and constant are applied in fp32.  Logits are fp32 sums of the exact bf16 products, the
+ * softmax in fp32 (exp2), the softmax weights rounded to bf16 for the value product, fp32 accumulation,
+ * bf16 output (round to nearest even).
  * Scratch (the stream's buffer): the normalised keys (B*L*C bf16) and r_q (B*N fp32).  Errors as above.
  */
 sana_status_t sana_cross_attn_fwd(const void* q, const void* k, const void* v, const float* gq, const float* gk,
