@@ -83,6 +83,21 @@ def test_cross_peaked_logits_norm_off(gpu_lib):
     _check(_run(gpu_lib, inp, norm=False), _ref(inp, norm=False), inp, "peaked")
 
 
+def test_cross_loose_bound_norm_on(gpu_lib):
+    """Norm on, with query 3 and text token 7 of every sample concentrated on one channel each of head 0
+    (channels 0 and 1, so the two are orthogonal): after the norm their head-0 parts have norms near
+    sqrt(C), so |q^| max|k^| bounds head 0's logits too loosely (2m > 64 in exponent units) and the
+    wave takes the exact-maximum pass, whose maximum then enters the MFMA as the subtracted constant,
+    while the logits themselves stay moderate."""
+    inp = gen_cross(40, 2, 300, L=120, H=8, ragged=True)
+    inp.q[:, 3, :32] = 0.0
+    inp.q[:, 3, 0] = 60.0
+    inp.k[:, 7, :32] = 0.0
+    inp.k[:, 7, 1] = 60.0
+    assert (inp.kv_len > 7).all()
+    _check(_run(gpu_lib, inp), _ref(inp), inp, "loose bound, norm on")
+
+
 def test_cross_zero_valid_tokens_gives_zeros(gpu_lib):
     """kv_len 0 (not defined by the oracle, which requires >= 1): the library writes zeros."""
     inp = gen_cross(36, 2, 64, L=20, H=2)
