@@ -77,10 +77,14 @@ hipError_t launch_relayout_k32(const uint16_t* x, int64_t M, int K, uint16_t* xb
 // qkv[M, 3C] = x[M, C] @ w[C, 3C], bf16 in / bf16 out (fp32 accumulation); xb is x K-blocked
 // (launch_relayout_k32), w row-major.  With k_ssq set, the blocks
 // whose columns overlap the K block [C, 2C) also write, per row, the sum of squares of the bf16 outputs
-// they hold in that block: k_ssq[m * qkv_gemm_k_parts(C) + j] for the j-th such column panel.
+// they hold in that block: k_ssq[m * qkv_gemm_k_parts(C, gemm_wide(M, 3C)) + j] for the j-th such
+// column panel.
 hipError_t launch_qkv_gemm(const uint16_t* xb, const uint16_t* w, uint16_t* qkv, int64_t M, int C,
                            hipStream_t stream, float* k_ssq = nullptr);
-int qkv_gemm_k_parts(int C);
+// Whether a bf16 GEMM of M rows by NO output columns runs on 256-column blocks (else 192).
+bool gemm_wide(int64_t M, int NO);
+// Column panels of the K block [C, 2C) for the given block width (the int8 form: wide = false).
+int qkv_gemm_k_parts(int C, bool wide);
 // W8A8 form: xq int8 K-blocked [C/64][M][64] (launch_quant_rows with k_blocked) with per-row scales
 // s_x [M]; wt int8 K-blocked [C/64][3C][64] (launch_pack_k64 of W transposed, [3C, C]) with per-column
 // scales s_w [3C]; qkv = bf16((sum_c xq*wt) * s_x[m] * s_w[n]).

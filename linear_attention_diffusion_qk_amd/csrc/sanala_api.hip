@@ -302,7 +302,7 @@ extern "C" sana_status_t sana_qkv_linear_attn_fwd(const void* x, const void* Wqk
   // With the QK-Norm on, the projection's epilogue also leaves per-row partial sums of squares of K,
   // which replace the attention's row-statistics pass over K.
   const size_t qkv_bytes = ((size_t)M * 3 * C * 2 + 255) / 256 * 256;
-  const int k_parts = norm ? sanala::qkv_gemm_k_parts((int)C) : 0;
+  const int k_parts = norm ? sanala::qkv_gemm_k_parts((int)C, sanala::gemm_wide(M, 3 * (int)C)) : 0;
   const size_t ssq_bytes = ((size_t)M * k_parts * 4 + 255) / 256 * 256;
   const size_t xb_bytes = ((size_t)M * C * 2 + 255) / 256 * 256;  // x K-blocked for the GEMM
   ScratchLease lease;
@@ -437,7 +437,7 @@ extern "C" sana_status_t sana_qkv_w8a8_linear_attn_fwd(const void* x, const void
   const size_t xq_bytes = ((size_t)M * C + 255) / 256 * 256;
   const size_t sx_bytes = ((size_t)M * 4 + 255) / 256 * 256;
   const size_t qkv_bytes = ((size_t)M * 3 * C * 2 + 255) / 256 * 256;
-  const int k_parts = norm ? sanala::qkv_gemm_k_parts((int)C) : 0;
+  const int k_parts = norm ? sanala::qkv_gemm_k_parts((int)C, false) : 0;  // the int8 GEMM's panels
   const size_t ssq_bytes = ((size_t)M * k_parts * 4 + 255) / 256 * 256;
   ScratchLease lease;
   if (lease.acquire(dev, stream, xq_bytes + sx_bytes + qkv_bytes + ssq_bytes + plan.ws_bytes) != hipSuccess)
