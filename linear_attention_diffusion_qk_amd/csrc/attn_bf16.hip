@@ -46,7 +46,7 @@ namespace sanala {
 constexpr int kStateSB = 64;     // tokens per sub-block
 constexpr int kStatePitch = 72;  // bf16 per staged row (64 used)
 
-template <bool NORM, bool F16>
+template <bool NORM, bool F16, bool NTV = false>
 __device__ __forceinline__ void chunk_state(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t ld,
                                             const float* __restrict__ r_k, const float* __restrict__ gk, int N, int H,
                                             int b, int p, int c, int Tc, uint16_t* Ks, uint16_t* Vs, float* rs,
@@ -78,7 +78,10 @@ __device__ __forceinline__ void chunk_state(const uint16_t* __restrict__ k, cons
       if (n < n_end && (cu >> 2) < nh) {
         const int64_t off = (row0 + n) * ld + h0 * kHeadDim + cu * 8;
         pk[it] = load16(k + off);
-        pv[it] = load16(v + off);
+        if constexpr (NTV)
+          pv[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + off));
+        else
+          pv[it] = load16(v + off);
       }
     }
     if (tid < SB) pr = (NORM && n0 + tid < n_end) ? r_k[row0 + n0 + tid] : 1.0f;  // rows past the end are zero
@@ -277,7 +280,7 @@ __device__ __forceinline__ void reduce_slice(const float* __restrict__ part, uin
 // sequence: the block writes the operands itself.  Several: with flags set, the chunk rendezvous above;
 // otherwise the block writes its partial for kv_reduce_bf16.
 // ---------------------------------------------------------------------------------------------
-template <bool NORM, bool F16>
+template <bool NORM, bool F16, bool NTV = false>
 __global__ __launch_bounds__(256, 5) void kv_state_bf16(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                      int64_t ld, const float* __restrict__ r_k,
                                                      const float* __restrict__ gq, const float* __restrict__ gk,
@@ -292,7 +295,7 @@ __global__ __launch_bounds__(256, 5) void kv_state_bf16(const uint16_t* __restri
 
   const int c = blockIdx.x, p = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
-  chunk_state<NORM, F16>(k, v, ld, r_k, gk, N, H, b, p, c, Tc, Ks, Vs, rs, fin);
+  chunk_state<NORM, F16, NTV>(k, v, ld, r_k, gk, N, H, b, p, c, Tc, Ks, Vs, rs, fin);
   const int h0 = 2 * p;
   const int nh = min(2, H - h0);
   const int64_t bh0 = (int64_t)b * H + h0;
@@ -740,13 +743,15 @@ static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t l
   const bool rdv = p.rendezvous && !xchg;
   uint32_t* flags = rdv ? reinterpret_cast<uint32_t*>(base + p.off_flags) : nullptr;
   const uint32_t epoch = rdv ? next_epoch() : 0u;
+  const bool ntv = p.nt_v;  // non-temporal V loads (the planner's choice)
   if (xchg) {
   } else if (p.norm)
-    launch_kernel("kv_state", kv_state_bf16<true, F16>, grid, 256, 0, stream, k, v, ldkv, r_k, gq, gk, N, H, p.Tc, p.NC,
-                  part, Sop, zop, gsg, flags, epoch, p.xchg_spin);
+    launch_kernel("kv_state", ntv ? kv_state_bf16<true, F16, true> : kv_state_bf16<true, F16, false>, grid, 256, 0,
+                  stream, k, v, ldkv, r_k, gq, gk, N, H, p.Tc, p.NC, part, Sop, zop, gsg, flags, epoch, p.xchg_spin);
   else
-    launch_kernel("kv_state", kv_state_bf16<false, F16>, grid, 256, 0, stream, k, v, ldkv, nullptr, nullptr, nullptr, N,
-                  H, p.Tc, p.NC, part, Sop, zop, gsg, flags, epoch, p.xchg_spin);
+    launch_kernel("kv_state", ntv ? kv_state_bf16<false, F16, true> : kv_state_bf16<false, F16, false>, grid, 256, 0,
+                  stream, k, v, ldkv, nullptr, nullptr, nullptr, N, H, p.Tc, p.NC, part, Sop, zop, gsg, flags, epoch,
+                  p.xchg_spin);
   if (p.NC > 1 && !rdv) {
     const unsigned blocks = (unsigned)((BH * kPartStride + 255) / 256);
     if (p.norm)

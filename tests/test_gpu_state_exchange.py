@@ -62,3 +62,20 @@ def test_exchange_repeats_bitwise_across_calls(gpu_lib):
     outs = [_with_env({"SANA_STATE_XCHG": "1"}, lambda: _run(gpu_lib, inp)) for _ in range(3)]
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+@pytest.mark.parametrize("case", ["b32_n1024", "b4_n1000_f16", "b2_n777_norm_off", "b1_n4096"])
+def test_state_pass_v_load_forms_agree_bitwise(gpu_lib, case):
+    """Non-temporal V loads in the state pass (the planner's choice for a batch with one chunk per
+    sample; SANA_STATE_NT_V forces either form) change only the loads' cache policy: the output must be
+    the same bit for bit, and within the oracle's gates."""
+    inp = {"b32_n1024": lambda: gen_config(3),
+           "b4_n1000_f16": lambda: gen_attn(7401, 4, 1000, dtype="f16"),
+           "b2_n777_norm_off": lambda: gen_attn(7402, 2, 777, dtype="bf16", norm=False),
+           "b1_n4096": lambda: gen_attn(7403, 1, 4096, dtype="bf16")}[case]()
+    print(f"[nt-v] {case}", flush=True)
+    outs = [_with_env({"SANA_STATE_NT_V": f}, lambda: _run(gpu_lib, inp)) for f in ("0", "1")]
+    bits = torch.int16
+    assert torch.equal(outs[0].view(bits), outs[1].view(bits)), case
+    if case != "b32_n1024":  # the 32-sample batch is checked against the oracle elsewhere
+        check(outs[1], oracle_out(inp), inp.v, inp.dtype, f"nt-v {case}")
