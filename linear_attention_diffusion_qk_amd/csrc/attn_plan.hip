@@ -131,13 +131,15 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
     const bool on = s && s[0] == '1' && s[1] == 0;
     p.rendezvous = bf && p.NC > 1 && p.NC <= 16 && (int64_t)B * groups * p.NC <= 5 * (int64_t)p.num_cus && on;
   }
-  // Non-temporal V loads in the 16-bit state pass for a batch whose samples are one chunk each (measured
-  // on MI355X: the 32 x 1024-token batch 139.7 -> 134.6 us per call, through a faster output kernel; the
-  // 4K call 66.4 -> 67.7 us, so long samples keep ordinary loads).  SANA_STATE_NT_V=0 or 1 forces it.
+  // Non-temporal V loads in the 16-bit state pass for a batch of several samples (measured on MI355X,
+  // through a faster output kernel: the 32 x 1024-token batch 139.7 -> 134.6 us per call, the 2K fused
+  // front end (4 x 4096) 542.7 -> 537.7 us, its W8A8 form 402.0 -> 394.5 us; a single 1024-token sample
+  // unchanged, the single 16384-token sample 66.4 -> 67.7 us, so single samples keep ordinary loads).
+  // SANA_STATE_NT_V=0 or 1 forces either form.
   {
     const char* s = std::getenv("SANA_STATE_NT_V");
     const bool forced = s && (s[0] == '0' || s[0] == '1') && s[1] == 0;
-    p.nt_v = bf && !p.state_xchg && (forced ? s[0] == '1' : (B > 1 && p.NC == 1));
+    p.nt_v = bf && !p.state_xchg && (forced ? s[0] == '1' : B > 1);
   }
   {
     const char* s = std::getenv("SANA_XCHG_SPIN_US");
