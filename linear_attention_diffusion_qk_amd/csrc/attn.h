@@ -36,7 +36,7 @@ struct AttnPlan {
   int num_cus;          // compute units of the current device
   bool state_xchg;      // 16-bit, QK-Norm on, r_q in the output kernel: r_k formed inside the state pass
   bool rendezvous;      // 16-bit, NC > 1: the state blocks reduce the chunk partials among themselves
-  bool nt_v;            // 16-bit state pass reads V with non-temporal loads (batches of several samples)
+  bool nt_v;            // 16-bit path reads K and V with non-temporal loads (batches of several samples)
   uint32_t xchg_spin;   // wait limit of the cross-block waits (exchange, rendezvous), 100 MHz ticks
   size_t off_rk, off_rq, off_part, off_S32, off_z, off_Sop, off_xchg, off_flags;
   size_t ws_bytes;

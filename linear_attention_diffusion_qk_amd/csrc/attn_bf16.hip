@@ -77,7 +77,10 @@ __device__ __forceinline__ void chunk_state(const uint16_t* __restrict__ k, cons
       pv[it] = u32x4{0u, 0u, 0u, 0u};
       if (n < n_end && (cu >> 2) < nh) {
         const int64_t off = (row0 + n) * ld + h0 * kHeadDim + cu * 8;
-        pk[it] = load16(k + off);
+        if constexpr (NTV)
+          pk[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + off));
+        else
+          pk[it] = load16(k + off);
         if constexpr (NTV)
           pv[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + off));
         else
@@ -736,14 +739,15 @@ static hipError_t launch_attn_16(const AttnPlan& p, const uint16_t* q, int64_t l
     launch_kernel("rowfinish_k", rowfinish_kernel, (unsigned)((rows + 255) / 256), 256, 0, stream, k_ssq, k_parts, rows,
                   inv_C, eps, r_k);
   else if (p.norm)
-    launch_kernel("rowstats_k", rowstats_kernel<uint16_t, F16>, rs_blocks, 256, 0, stream, k, ldkv, rows, C, eps, r_k,
+    launch_kernel("rowstats_k", p.nt_v ? rowstats_kernel<uint16_t, F16, true> : rowstats_kernel<uint16_t, F16>,
+                  rs_blocks, 256, 0, stream, k, ldkv, rows, C, eps, r_k,
                   nullptr, 0, nullptr);
   const dim3 grid(p.NC, (H + 1) / 2, B);
   // Several chunks: reduced by the state blocks themselves (rendezvous) or by kv_reduce_bf16.
   const bool rdv = p.rendezvous && !xchg;
   uint32_t* flags = rdv ? reinterpret_cast<uint32_t*>(base + p.off_flags) : nullptr;
   const uint32_t epoch = rdv ? next_epoch() : 0u;
-  const bool ntv = p.nt_v;  // non-temporal V loads (the planner's choice)
+  const bool ntv = p.nt_v;  // non-temporal K and V loads (the planner's choice)
   if (xchg) {
   } else if (p.norm)
     launch_kernel("kv_state", ntv ? kv_state_bf16<true, F16, true> : kv_state_bf16<true, F16, false>, grid, 256, 0,

@@ -131,10 +131,12 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
     const bool on = s && s[0] == '1' && s[1] == 0;
     p.rendezvous = bf && p.NC > 1 && p.NC <= 16 && (int64_t)B * groups * p.NC <= 5 * (int64_t)p.num_cus && on;
   }
-  // Non-temporal V loads in the 16-bit state pass for a batch of several samples (measured on MI355X,
-  // through a faster output kernel: the 32 x 1024-token batch 139.7 -> 134.6 us per call, the 2K fused
-  // front end (4 x 4096) 542.7 -> 537.7 us, its W8A8 form 402.0 -> 394.5 us; a single 1024-token sample
-  // unchanged, the single 16384-token sample 66.4 -> 67.7 us, so single samples keep ordinary loads).
+  // For a batch of several samples, K and V are read with non-temporal loads (the row-statistics pass and
+  // the 16-bit state pass are their last readers), which leaves the caches to the Q rows the output pass
+  // reads.  Measured on MI355X, mostly through a faster output kernel: the 32 x 1024-token batch 139.7 ->
+  // 127.9 us per call (V alone: 134.6), the 2K fused front end 542.7 -> 537.7 us (V alone; K as well
+  // within 0.5% either way, also for its W8A8 form, 402.0 -> 394.5 us with V alone).  A single sample
+  // keeps ordinary loads (16384 tokens: 66.4 -> 67.7 us with V non-temporal; 1024 tokens unchanged).
   // SANA_STATE_NT_V=0 or 1 forces either form.
   {
     const char* s = std::getenv("SANA_STATE_NT_V");

@@ -65,10 +65,10 @@ def test_exchange_repeats_bitwise_across_calls(gpu_lib):
 
 
 @pytest.mark.parametrize("case", ["b32_n1024", "b4_n1000_f16", "b2_n777_norm_off", "b1_n4096"])
-def test_state_pass_v_load_forms_agree_bitwise(gpu_lib, case):
-    """Non-temporal V loads in the state pass (the planner's choice for a batch of several samples;
-    SANA_STATE_NT_V forces either form) change only the loads' cache policy: the output must be the same
-    bit for bit, and within the oracle's gates.  Cases: the 32-sample batch, a binary16 batch, a batch
+def test_kv_load_forms_agree_bitwise(gpu_lib, case):
+    """Non-temporal K and V loads in the row-statistics and state passes (the planner's choice for a
+    batch of several samples; SANA_STATE_NT_V forces either form) change only the loads' cache policy:
+    the output must be the same bit for bit, and within the oracle's gates.  Cases: the 32-sample batch, a binary16 batch, a batch
     with the norm off, a single sample (where the default is the ordinary form)."""
     inp = {"b32_n1024": lambda: gen_config(3),
            "b4_n1000_f16": lambda: gen_attn(7401, 4, 1000, dtype="f16"),
