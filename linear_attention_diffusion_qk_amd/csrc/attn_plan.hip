@@ -131,12 +131,11 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
     const bool on = s && s[0] == '1' && s[1] == 0;
     p.rendezvous = bf && p.NC > 1 && p.NC <= 16 && (int64_t)B * groups * p.NC <= 5 * (int64_t)p.num_cus && on;
   }
-  // For a batch of several samples, K and V are read with non-temporal loads (the row-statistics pass and
-  // the 16-bit state pass are their last readers), which leaves the caches to the Q rows the output pass
-  // reads.  Measured on MI355X, mostly through a faster output kernel: the 32 x 1024-token batch 139.7 ->
-  // 127.9 us per call (V alone: 134.6), the 2K fused front end 542.7 -> 537.7 us (V alone; K as well
-  // within 0.5% either way, also for its W8A8 form, 402.0 -> 394.5 us with V alone).  A single sample
-  // keeps ordinary loads (16384 tokens: 66.4 -> 67.7 us with V non-temporal; 1024 tokens unchanged).
+  // For a batch of several samples, K and V are read with non-temporal loads: the row-statistics pass and
+  // the 16-bit state pass are their last readers, and the output pass then finds more of Q in the caches.
+  // Measured on MI355X: the 32 x 1024-token batch 139.7 -> 127.9 us per call (output kernel 61.3 -> 48
+  // us), the 2K fused front end 542.7 -> 537.7 us and its W8A8 form 402.0 -> 394.5 us.  A single sample
+  // keeps ordinary loads (16384 tokens: 66.4 -> 67.7 us with V non-temporal; 1024 tokens: unchanged).
   // SANA_STATE_NT_V=0 or 1 forces either form.
   {
     const char* s = std::getenv("SANA_STATE_NT_V");

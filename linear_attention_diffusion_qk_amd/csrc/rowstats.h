@@ -8,7 +8,8 @@ namespace sanala {
 // r[row] = 1 / sqrt(mean_c x[row, c]^2 + eps) over all C channels of a token row (the QK-Norm
 // scale), one wave per row, 16-byte loads (16-bit T: bf16, or binary16 with F16).  Rows are `ld` elements apart.
 // With x1 given, the launch covers 2 * rows rows: the second half are the rows of x1 (stride ld1)
-// and their scales go to r1 (K and Q in one launch).  NT: the rows are read with non-temporal loads.
+// and their scales go to r1 (K and Q in one launch).  NT: rows of up to 64 * MAXU units are read with
+// non-temporal loads.
 template <typename T, bool F16 = false, bool NT = false>
 __global__ __launch_bounds__(256) void rowstats_kernel(const T* __restrict__ x, int64_t ld, int64_t rows, int C,
                                                        float eps, float* __restrict__ r,
