@@ -36,13 +36,14 @@ struct AttnPlan {
   int num_cus;          // compute units of the current device
   bool state_xchg;      // 16-bit, QK-Norm on, r_q in the output kernel: r_k formed inside the state pass
   bool rendezvous;      // 16-bit, NC > 1: the state blocks reduce the chunk partials among themselves
-  bool nt_v;            // 16-bit path reads K and V with non-temporal loads (batches of several samples)
+  bool nt_v;            // 16-bit path reads K and V with non-temporal loads (see plan_attn)
   uint32_t xchg_spin;   // wait limit of the cross-block waits (exchange, rendezvous), 100 MHz ticks
   size_t off_rk, off_rq, off_part, off_S32, off_z, off_Sop, off_xchg, off_flags;
   size_t ws_bytes;
 };
 
-AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm);
+// fused: q, k and v come from the projection in front of the attention (the library's own scratch).
+AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm, bool fused = false);
 
 // q is read with row stride ldq, k and v with ldkv, out written with ldo (all in elements).
 // k_ssq (bf16 path only, optional): per-row partial sums of squares of K in k_parts column panels,

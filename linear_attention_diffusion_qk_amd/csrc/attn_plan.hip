@@ -38,7 +38,7 @@ uint32_t next_epoch() {
   return e;
 }
 
-AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
+AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm, bool fused) {
   AttnPlan p{};
   p.B = B;
   p.N = N;
@@ -131,16 +131,18 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm) {
     const bool on = s && s[0] == '1' && s[1] == 0;
     p.rendezvous = bf && p.NC > 1 && p.NC <= 16 && (int64_t)B * groups * p.NC <= 5 * (int64_t)p.num_cus && on;
   }
-  // For a batch of several samples, K and V are read with non-temporal loads: the row-statistics pass and
-  // the 16-bit state pass are their last readers, and the output pass then finds more of Q in the caches.
-  // Measured on MI355X: the 32 x 1024-token batch 139.7 -> 127.9 us per call (output kernel 61.3 -> 48
-  // us), the 2K fused front end 542.7 -> 537.7 us and its W8A8 form 402.0 -> 394.5 us.  A single sample
-  // keeps ordinary loads (16384 tokens: 66.4 -> 67.7 us with V non-temporal; 1024 tokens: unchanged).
-  // SANA_STATE_NT_V=0 or 1 forces either form.
+  // K and V are read with non-temporal loads (the row-statistics pass and the 16-bit state pass are their
+  // last readers, and the output pass then finds more of Q in the caches) when together they exceed the
+  // 256 MB Infinity Cache, and behind the fused projection.  Measured on MI355X, per call, ordinary ->
+  // non-temporal: 32 x 1024 tokens 139.7 -> 127.9 us, 2 x 16384 129.8 -> 123.5, 4 x 8192 136.1 -> 134.3,
+  // the 2K fused front end (4 x 4096) 542.7 -> 537.7 and its W8A8 form 402.0 -> 394.5; below the cache
+  // size the other way: 1 x 16384 66.4 -> 67.7, 8 x 2048 73.9 -> 76.6, 2 x 4096 42.5 -> 43.8, and a
+  // single 1024-token sample unchanged.  SANA_STATE_NT_V=0 or 1 forces either form.
   {
     const char* s = std::getenv("SANA_STATE_NT_V");
     const bool forced = s && (s[0] == '0' || s[0] == '1') && s[1] == 0;
-    p.nt_v = bf && !p.state_xchg && (forced ? s[0] == '1' : B > 1);
+    const double kv_bytes = 2.0 * (double)B * N * H * kHeadDim * (dtype == kDtypeF32 ? 4 : 2);
+    p.nt_v = bf && !p.state_xchg && (forced ? s[0] == '1' : (fused || kv_bytes > 256.0 * 1024 * 1024));
   }
   {
     const char* s = std::getenv("SANA_XCHG_SPIN_US");

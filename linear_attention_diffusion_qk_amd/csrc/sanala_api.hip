@@ -298,7 +298,7 @@ extern "C" sana_status_t sana_qkv_linear_attn_fwd(const void* x, const void* Wqk
   init_pool(dev);
   g_timing.count = 0;
   const bool norm = gq != nullptr;
-  const sanala::AttnPlan plan = sanala::plan_attn(B, N, H, sanala::kDtypeBf16, norm);
+  const sanala::AttnPlan plan = sanala::plan_attn(B, N, H, sanala::kDtypeBf16, norm, true);
   // With the QK-Norm on, the projection's epilogue also leaves per-row partial sums of squares of K,
   // which replace the attention's row-statistics pass over K.
   const size_t qkv_bytes = ((size_t)M * 3 * C * 2 + 255) / 256 * 256;
@@ -432,7 +432,7 @@ extern "C" sana_status_t sana_qkv_w8a8_linear_attn_fwd(const void* x, const void
   init_pool(dev);
   g_timing.count = 0;
   const bool norm = gq != nullptr;
-  const sanala::AttnPlan plan = sanala::plan_attn(B, N, H, sanala::kDtypeBf16, norm);
+  const sanala::AttnPlan plan = sanala::plan_attn(B, N, H, sanala::kDtypeBf16, norm, true);
   // Stream-ordered scratch: int8 x and its row scales, the bf16 qkv, the K row partial sums of squares.
   const size_t xq_bytes = ((size_t)M * C + 255) / 256 * 256;
   const size_t sx_bytes = ((size_t)M * 4 + 255) / 256 * 256;

@@ -66,10 +66,11 @@ def test_exchange_repeats_bitwise_across_calls(gpu_lib):
 
 @pytest.mark.parametrize("case", ["b32_n1024", "b4_n1000_f16", "b2_n777_norm_off", "b1_n4096"])
 def test_kv_load_forms_agree_bitwise(gpu_lib, case):
-    """Non-temporal K and V loads in the row-statistics and state passes (the planner's choice for a
-    batch of several samples; SANA_STATE_NT_V forces either form) change only the loads' cache policy:
-    the output must be the same bit for bit, and within the oracle's gates.  Cases: the 32-sample batch, a binary16 batch, a batch
-    with the norm off, a single sample (where the default is the ordinary form)."""
+    """Non-temporal K and V loads in the row-statistics and state passes (the planner's choice when K and
+    V together exceed the Infinity Cache, and behind the fused projection; SANA_STATE_NT_V forces either
+    form) change only the loads' cache policy: the output must be the same bit for bit, and within the
+    oracle's gates.  Cases: the 32-sample batch (non-temporal by default), a binary16 batch, a batch with
+    the norm off, a single sample (ordinary by default)."""
     inp = {"b32_n1024": lambda: gen_config(3),
            "b4_n1000_f16": lambda: gen_attn(7401, 4, 1000, dtype="f16"),
            "b2_n777_norm_off": lambda: gen_attn(7402, 2, 777, dtype="bf16", norm=False),
