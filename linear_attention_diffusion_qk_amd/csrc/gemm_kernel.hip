@@ -372,11 +372,13 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(const void* __restri
   __syncthreads();
   const int rows = min(BM, M - m0), cols = min(Geo<NT>::BN, NO - n0);  // cols: a multiple of 8
   if constexpr (Y_BLK) {
-    // Chunk j of the tile: rows x 64 bytes, consecutive in y.
+    // Chunk j of the tile: rows x 64 bytes, consecutive in y.  Non-temporal: the Mix-FFN's expanded
+    // activations (367 MB on the 2K grid) exceed the Infinity Cache and are read once, by the conv
+    // (Mix-FFN call 1208.0 -> 1203.9 us on MI355X, bitwise-equal output).
     for (int i = tid; i < (Geo<NT>::BN / 32) * BM * 4; i += kThreads) {
       const int j = i / (BM * 4), r = (i / 4) % BM, w = i & 3;
       if (r < rows && 32 * j < cols)
-        store16(y + ((((int64_t)(n0 >> 5) + j) * M + m0 + r) << 5) + 8 * w, img_load16<NT>(obuf, r, 4 * j + w));
+        store16_nt(y + ((((int64_t)(n0 >> 5) + j) * M + m0 + r) << 5) + 8 * w, img_load16<NT>(obuf, r, 4 * j + w));
     }
   } else {
     for (int i = tid; i < BM * (Geo<NT>::BN / 8); i += kThreads) {
