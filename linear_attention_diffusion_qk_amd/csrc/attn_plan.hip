@@ -51,10 +51,13 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm, bool fused) {
   // of the K+V traffic).  16-bit state kernel (block = head pair x chunk, five resident per CU): the
   // chunk length minimising a cost model fitted to MI355X measurements -- a block streams 256 bytes per
   // token at about 12 GB/s, a CU at about 23 GB/s, and a split sequence adds the reduction (a launch of
-  // about 6 us plus 0.2 us per chunk).  It picks 14 chunks of 1216 tokens on the 4K workload (73-75 us
-  // per call against 75-77 us for 29 of 576, and 77.8 us for 15 of 1152, whose 525 blocks leave 13 CUs
-  // a third chunk), one chunk per sample for the 32-sample 1024-token batch (no reduction), and 8
-  // chunks of 128 for a single 1024-token sample.
+  // about 6 us plus 0.2 us per chunk, plus 0.0045 us per (sample, head) state beyond 280: the reduction
+  // takes 4-5 us up to 4 samples of 70 heads, but 12.8 us for 30 samples in 4 chunks and 14 us for 32 in
+  // 2; without that term 16 and 30 samples of 1024 tokens were split into 4 chunks of 256, 77.3 and
+  // 137.3 us per call against 68.8 and 124.8 us unsplit).  It picks 14 chunks of 1216 tokens on the 4K
+  // workload (73-75 us per call against 75-77 us for 29 of 576, and 77.8 us for 15 of 1152, whose 525
+  // blocks leave 13 CUs a third chunk), one chunk per sample for batches of 1024-token samples (no
+  // reduction), and 8 chunks of 128 for a single 1024-token sample.
   const int groups = bf ? (H + 1) / 2 : H;
   const int64_t per_chunk = (int64_t)B * groups;
   const int n64 = (N + 63) / 64 * 64;
@@ -69,7 +72,8 @@ AttnPlan plan_attn(int B, int N, int H, int dtype, bool norm, bool fused) {
       const int64_t blocks = per_chunk * nc;
       const int64_t per_cu = (blocks + p.num_cus - 1) / p.num_cus;
       const double stream_us = std::max(0.021 * t, 0.0111 * (double)per_cu * t);
-      const double cost = stream_us + (nc > 1 ? 6.0 + 0.2 * (double)nc : 0.0);
+      const double heads_beyond = std::max(0.0, (double)B * H - 280.0);
+      const double cost = stream_us + (nc > 1 ? 6.0 + 0.2 * (double)nc + 0.0045 * heads_beyond : 0.0);
       if (cost < best) {
         best = cost;
         Tc = t;
